@@ -1,0 +1,246 @@
+"""Dense fp64 definition of scaled-dot-product attention (test infrastructure).
+
+Every function here follows the definition on the pages directly; nothing is
+tiled, fused or reordered.  Inputs are the exact values of the stored arrays as
+float64 (bf16 bits or fp32 widened without change).
+
+Sources (page title, section):
+* "Transformer Architecture Breakdown" (airsota.com), section 1.2: the attention
+  formula softmax(Q K^T / sqrt(d_k) + M) V; Key Topic 5: the causal mask sets
+  entries with j > i to minus infinity; section 3.1 and section 5: RoPE rotates
+  adjacent pairs (x_2j, x_2j+1) by the angle m * theta_j.
+* "coding-interview attention from scratch" (arganzheng.life), section 三.1:
+  stable softmax and log-softmax via the row max; 三.2: masked scores become
+  minus infinity so their weight is exactly zero; 三.4: query head h reads KV head
+  h // (H / H_kv); 三.5: theta_i = base^(-2i/d), positions 0..T-1, even/odd pairs,
+  V is not rotated; 三.6: a decode step attends the new query to every cached key
+  without a mask; 八 question 5: with t new queries over len cached keys the
+  visible set is [all of the cache | lower triangle], i.e. bottom-right aligned.
+* "Attention mechanisms: from alignment to efficient long context"
+  (fahimfaisal.info), Notation: n_q x n_k score matrix, h query heads, h_kv KV
+  heads; section 9: the group index of a query head is h // (h / h_kv).
+
+Readings where the pages are silent (each listed in the design notes):
+* O and logsumexp are returned in float64 here; the GPU writes them as fp32.
+* With RoPE on, the rotated Q and K are rounded back to the input dtype
+  (fp64 -> fp32 -> bf16, each round-to-nearest-even) before the product, as a
+  bf16 -> bf16 operator would; V is never rotated.
+* theta_j = pow(base, -2j/d) for j = 0..d/2-1 with the C library ``pow``; the
+  angle is the fp64 product position * theta_j; cos and sin are the C library's
+  fp64 ``cos`` and ``sin`` (Python ``math``).
+* Query i sits at position Nk - Nq + i, key j at position j; causal visibility
+  is j <= Nk - Nq + i.
+* logsumexp is the natural-log logsumexp of the visible scaled scores of a row.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+# ------------------------------------------------------------------ softmax
+def softmax(x: np.ndarray) -> np.ndarray:
+    """Row softmax with the row max subtracted first.
+
+    "coding-interview attention from scratch", section 三.1: subtracting the row
+    max leaves the result unchanged and keeps exp from overflowing.  Entries that
+    are -inf get weight exactly 0.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m = np.max(x, axis=-1, keepdims=True)
+    e = np.exp(x - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def logsumexp(x: np.ndarray) -> np.ndarray:
+    """Natural-log logsumexp of each row: m + log(sum exp(x - m)).
+
+    Same page, section 三.1 (log-softmax is x minus this quantity).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m = np.max(x, axis=-1, keepdims=True)
+    return (m + np.log(np.sum(np.exp(x - m), axis=-1, keepdims=True)))[..., 0]
+
+
+# ------------------------------------------------------------------ rounding
+def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round fp64 values to the storage dtype and return them as fp64.
+
+    ``"f64"``: unchanged; ``"f32"``: fp64 -> fp32 (round to nearest even);
+    ``"bf16"``: fp64 -> fp32 -> bf16, each step round to nearest even.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == "f64":
+        return x.copy()
+    x32 = x.astype(np.float32)
+    if dtype == "f32":
+        return x32.astype(np.float64)
+    if dtype != "bf16":
+        raise ValueError(dtype)
+    u = x32.view(np.uint32).astype(np.uint64)
+    # keep the upper 16 bits after adding half an ulp, ties going to the even one
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u32 = (u << 16).astype(np.uint32)
+    return u32.view(np.float32).astype(np.float64)
+
+
+# ------------------------------------------------------------------ RoPE
+_COS_SIN_CACHE: dict = {}
+
+
+def rope_cos_sin(n_pos: int, d: int, base: float):
+    """fp64 cos/sin of position * theta_j for positions 0..n_pos-1, j = 0..d/2-1.
+
+    "Transformer Architecture Breakdown", section 3.1 (frequencies
+    theta_j = base^(-2j/d)); "coding-interview attention from scratch", 三.5.
+    Each value comes from ``math.cos`` / ``math.sin`` of the fp64 product.
+    """
+    if d % 2:
+        raise ValueError("RoPE needs an even head dimension")
+    key = (int(n_pos), int(d), float(base))
+    hit = _COS_SIN_CACHE.get(key)
+    if hit is not None:
+        return hit
+    theta = [math.pow(base, -2.0 * j / d) for j in range(d // 2)]
+    cos = np.empty((n_pos, d // 2), dtype=np.float64)
+    sin = np.empty((n_pos, d // 2), dtype=np.float64)
+    for j, th in enumerate(theta):
+        ang = [float(p) * th for p in range(n_pos)]
+        cos[:, j] = [math.cos(a) for a in ang]
+        sin[:, j] = [math.sin(a) for a in ang]
+    _COS_SIN_CACHE.clear()  # keep at most one table alive
+    _COS_SIN_CACHE[key] = (cos, sin)
+    return cos, sin
+
+
+def rope(x: np.ndarray, positions: np.ndarray, base: float, dtype: str) -> np.ndarray:
+    """Rotate adjacent pairs of the last axis and round to ``dtype``.
+
+    x: [..., n, d] fp64 with row r of the n axis at ``positions[r]``.  Pair j of a
+    row at position p becomes (x0 cos a - x1 sin a, x0 sin a + x1 cos a) with
+    a = p * theta_j ("Transformer Architecture Breakdown", section 3.1 rotation
+    matrix and section 5; "coding-interview attention from scratch", 三.5).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    positions = np.asarray(positions, dtype=np.int64)
+    cos_t, sin_t = rope_cos_sin(int(positions.max()) + 1, d, base)
+    c = cos_t[positions]
+    s = sin_t[positions]
+    x0 = x[..., 0::2]
+    x1 = x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return round_to_dtype(out, dtype)
+
+
+# ------------------------------------------------------------------ attention
+def _f64(x) -> np.ndarray:
+    """Exact fp64 values of an array slice; uint16 arrays are read as bf16 bits."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def _kv_head(h: int, Hq: int, Hkv: int) -> int:
+    """Query head h reads KV head h // (Hq / Hkv) (repeat-interleave grouping)."""
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return h // (Hq // Hkv)
+
+
+def scores_and_weights(q_rows, k, *, scale, causal, q_pos, k_pos):
+    """Scaled scores S (masked entries -inf) and softmax weights P for some rows.
+
+    q_rows [r, d] at positions q_pos, k [n, d] at positions k_pos.  A key is
+    visible to a query when not causal or when its position is <= the query's.
+    """
+    s = (np.asarray(q_rows, np.float64) @ np.asarray(k, np.float64).T) * scale
+    if causal:
+        vis = np.asarray(k_pos)[None, :] <= np.asarray(q_pos)[:, None]
+        s = np.where(vis, s, -np.inf)
+    return s, softmax(s)
+
+
+def attention_rows(q, k, v, b: int, h: int, rows, *, causal: bool, scale: float,
+                   rope_base: float = 0.0, dtype: str = "bf16", _kcache=None):
+    """O [len(rows), d] and lse [len(rows)] for query rows of head (b, h).
+
+    q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d]: fp32/fp64 arrays, or uint16 arrays of bf16
+    bits; only the slices needed are widened to fp64.
+    """
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    if causal and Nq > Nk:
+        raise ValueError("causal attention needs Nq <= Nk")
+    g = _kv_head(h, Hq, Hkv)
+    rows = np.asarray(rows, dtype=np.int64)
+    q_pos = rows + (Nk - Nq)
+    k_pos = np.arange(Nk)
+    qr = _f64(q[b, h, rows])
+    kg = _f64(k[b, g])
+    vg = _f64(v[b, g])
+    if rope_base:
+        qr = rope(qr, q_pos, rope_base, dtype)
+        key = (b, g)
+        if _kcache is not None and key in _kcache:
+            kg = _kcache[key]
+        else:
+            kg = rope(kg, k_pos, rope_base, dtype)
+            if _kcache is not None:
+                _kcache.clear()
+                _kcache[key] = kg
+    o = np.empty((len(rows), d), dtype=np.float64)
+    lse = np.empty(len(rows), dtype=np.float64)
+    panel = max(1, (1 << 24) // max(Nk, 1))  # ~128 MB of fp64 scores per panel
+    for s0 in range(0, len(rows), panel):
+        sl = slice(s0, s0 + panel)
+        s, p = scores_and_weights(qr[sl], kg, scale=scale, causal=causal,
+                                  q_pos=q_pos[sl], k_pos=k_pos)
+        o[sl] = p @ vg
+        lse[sl] = logsumexp(s)
+    return o, lse
+
+
+def attention(q, k, v, *, causal: bool, scale: float, rope_base: float = 0.0,
+              dtype: str = "bf16"):
+    """Full O [B,Hq,Nq,d] and lse [B,Hq,Nq] (fp64) for every head and row."""
+    B, Hq, Nq, d = q.shape
+    o = np.empty((B, Hq, Nq, d), dtype=np.float64)
+    lse = np.empty((B, Hq, Nq), dtype=np.float64)
+    kc: dict = {}
+    for b in range(B):
+        for h in range(Hq):
+            o[b, h], lse[b, h] = attention_rows(
+                q, k, v, b, h, np.arange(Nq), causal=causal, scale=scale,
+                rope_base=rope_base, dtype=dtype, _kcache=kc)
+    return o, lse
+
+
+def decode(q, k_cache, v_cache, seq_lens, *, scale: float):
+    """One-query decode over a contiguous cache (no mask, no RoPE).
+
+    q [B,Hq,d]; caches [B,Hkv,max_len,d] (fp32/fp64, or uint16 bf16 bits);
+    sequence b uses cache rows
+    0..seq_lens[b]-1 ("coding-interview attention from scratch", 三.6).  A
+    sequence of length 0 has no visible key: O = 0 and lse = -inf.
+    """
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    o = np.zeros((B, Hq, d), dtype=np.float64)
+    lse = np.full((B, Hq), -np.inf, dtype=np.float64)
+    for b in range(B):
+        n = int(seq_lens[b])
+        if n == 0:
+            continue
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            s = (_f64(k_cache[b, g, :n]) @ _f64(q[b, h])) * scale
+            p = softmax(s)
+            o[b, h] = p @ _f64(v_cache[b, g, :n])
+            lse[b, h] = logsumexp(s)
+    return o, lse

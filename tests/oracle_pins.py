@@ -1,0 +1,356 @@
+"""Checks that tie the fp64 oracle to facts outside itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+something the pages or mathematics fix: a printed worked example, a closed
+form, an invariant, brute force on tiny inputs, or an independent library
+routine (torch's fp64 scaled_dot_product_attention and its bf16 conversion).
+They are collected by ``test_oracle.py`` and re-run against deliberately broken
+copies of the oracle by ``test_oracle_mutations.py``.
+
+Page titles used below:
+  [Breakdown]     "Transformer Architecture Breakdown" (airsota.com)
+  [Deconstructed] "Transformer Architecture Deconstructed" (byronfinn.github.io)
+  [Scratch]       "coding-interview attention from scratch" (arganzheng.life)
+  [Evolution]     "Attention mechanisms: from alignment to efficient long context"
+                  (fahimfaisal.info)
+"""
+
+from __future__ import annotations
+
+import cmath
+import math
+import os
+
+import numpy as np
+
+import oracle.dense as oa
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            out[key] = vals
+    return out
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _bf16_via_torch(x64):
+    """fp64 -> fp32 -> bf16 with torch's own conversions, back to fp64."""
+    import torch
+    t = torch.tensor(np.asarray(x64, np.float64))
+    return t.to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _rand_inputs(seed, B, Hq, Hkv, Nq, Nk, d, dtype, sigma=1.0):
+    """Small random inputs already representable in ``dtype``."""
+    r = _rng(seed)
+    q = r.standard_normal((B, Hq, Nq, d)) * sigma
+    k = r.standard_normal((B, Hkv, Nk, d)) * sigma
+    v = r.standard_normal((B, Hkv, Nk, d))
+    if dtype == "bf16":
+        q, k, v = (_bf16_via_torch(x) for x in (q, k, v))
+    elif dtype == "f32":
+        q, k, v = (x.astype(np.float32).astype(np.float64) for x in (q, k, v))
+    return q, k, v
+
+
+# ------------------------------------------------------------ brute force
+def _round_scalar(x, dtype):
+    if dtype == "f64":
+        return x
+    if dtype == "f32":
+        return float(np.float32(x))
+    return float(_bf16_via_torch(np.array([x]))[0])
+
+
+def _rot_complex(row, pos, base, dtype):
+    """RoPE of one row as complex multiplication: pair t is x_2t + i x_2t+1,
+    multiplied by e^(i pos theta_t), theta_t = base^(-2t/d) ([Breakdown] Key
+    Topic 4 and section 3.1)."""
+    d = len(row)
+    out = []
+    for t in range(d // 2):
+        z = complex(row[2 * t], row[2 * t + 1]) * cmath.exp(1j * (pos * base ** (-2.0 * t / d)))
+        out += [_round_scalar(z.real, dtype), _round_scalar(z.imag, dtype)]
+    return out
+
+
+def brute_attention(q, k, v, *, causal, scale, rope_base=0.0, dtype="f64"):
+    """Scalar-loop attention: for each query, exp-weights over visible keys.
+
+    Visibility for t = Nq new queries over Nk keys follows [Scratch] 八 question 5
+    (all earlier keys plus a lower triangle over the last Nq), query head h uses
+    KV head from the repeat-interleave list of [Scratch] 三.4.
+    """
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    group = [g for g in range(Hkv) for _ in range(Hq // Hkv)]
+    o = np.zeros((B, Hq, Nq, d))
+    lse = np.zeros((B, Hq, Nq))
+    for b in range(B):
+        for h in range(Hq):
+            g = group[h]
+            keys = [list(k[b, g, j]) for j in range(Nk)]
+            if rope_base:
+                keys = [_rot_complex(keys[j], j, rope_base, dtype) for j in range(Nk)]
+            for i in range(Nq):
+                qi = list(q[b, h, i])
+                pos = Nk - Nq + i
+                if rope_base:
+                    qi = _rot_complex(qi, pos, rope_base, dtype)
+                vis = [j for j in range(Nk) if (not causal) or j <= pos]
+                s = {j: scale * sum(qi[t] * keys[j][t] for t in range(d)) for j in vis}
+                m = max(s.values())
+                w = {j: math.exp(s[j] - m) for j in vis}
+                z = sum(w.values())
+                for t in range(d):
+                    o[b, h, i, t] = sum(w[j] * v[b, g, j, t] for j in vis) / z
+                lse[b, h, i] = m + math.log(z)
+    return o, lse
+
+
+# ------------------------------------------------------------ pins
+def pin_softmax_worked_example():
+    """[Scratch] 三.1 prints [0.090 0.245 0.665] for [1000, 1001, 1002]."""
+    g = _golden("softmax_worked_example.txt")
+    x = np.array([float(t) for t in g["input"]])
+    want = np.array([float(t) for t in g["stable"]])
+    got = oa.softmax(x[None, :])[0]
+    assert np.all(np.round(got, int(g["decimals"][0])) == want), got
+    with np.errstate(over="ignore", invalid="ignore"):
+        naive = np.exp(x) / np.exp(x).sum()
+    assert all(t == "nan" for t in g["naive"]) and np.all(np.isnan(naive))
+    assert abs(oa.logsumexp(x[None, :])[0] - (1002 + math.log(1 + math.exp(-1) + math.exp(-2)))) < 1e-12
+
+
+def pin_softmax_shift_invariance():
+    """Subtracting a constant from a row changes nothing ([Scratch] 三.1)."""
+    x = _rng(1).standard_normal((16, 33)) * 3
+    for c in (-7.5, 0.25, 40.0):
+        # x + c itself rounds (ulp of 40 is 7e-15), so allow a few ulps
+        assert np.max(np.abs(oa.softmax(x + c) - oa.softmax(x))) < 1e-13
+        assert np.max(np.abs(oa.logsumexp(x + c) - (oa.logsumexp(x) + c))) < 1e-12
+
+
+_SMALL = [
+    # B, Hq, Hkv, Nq, Nk, d, causal, rope_base, dtype
+    (1, 1, 1, 5, 5, 4, False, 0.0, "f64"),
+    (1, 2, 2, 6, 6, 8, True, 0.0, "f32"),
+    (2, 4, 2, 5, 7, 8, True, 10000.0, "bf16"),
+    (1, 4, 1, 3, 8, 6, False, 100.0, "bf16"),
+    (1, 3, 1, 7, 7, 4, True, 50.0, "f32"),
+    (1, 2, 1, 1, 6, 8, True, 10.0, "bf16"),
+]
+
+
+def pin_brute_force_small():
+    """Dense oracle = scalar loops (with complex-number RoPE) on tiny inputs."""
+    for n, (B, Hq, Hkv, Nq, Nk, d, causal, base, dt) in enumerate(_SMALL):
+        q, k, v = _rand_inputs(100 + n, B, Hq, Hkv, Nq, Nk, d, dt)
+        scale = 1.0 / math.sqrt(d)
+        o, lse = oa.attention(q, k, v, causal=causal, scale=scale, rope_base=base, dtype=dt)
+        ob, lb = brute_attention(q, k, v, causal=causal, scale=scale, rope_base=base, dtype=dt)
+        assert np.max(np.abs(o - ob)) < 1e-12, (n, np.max(np.abs(o - ob)))
+        assert np.max(np.abs(lse - lb)) < 1e-12, (n, np.max(np.abs(lse - lb)))
+
+
+def pin_torch_sdpa():
+    """O equals torch's fp64 scaled_dot_product_attention (enable_gqa), the library
+    routine [Scratch] 三.4 names for the comparison."""
+    import torch
+    import torch.nn.functional as F
+    cases = [(2, 8, 2, 33, 33, 16, True), (1, 4, 4, 17, 40, 32, False),
+             (1, 6, 1, 9, 9, 8, True), (2, 4, 2, 12, 30, 16, True)]
+    for n, (B, Hq, Hkv, Nq, Nk, d, causal) in enumerate(cases):
+        q, k, v = _rand_inputs(200 + n, B, Hq, Hkv, Nq, Nk, d, "f64")
+        scale = 1.0 / math.sqrt(d)
+        o, _ = oa.attention(q, k, v, causal=causal, scale=scale, dtype="f64")
+        mask = None
+        if causal:
+            # visible iff j <= i + (Nk - Nq): bottom-right causal
+            mask = torch.ones(Nq, Nk, dtype=torch.bool).tril(diagonal=Nk - Nq)
+        ot = F.scaled_dot_product_attention(
+            torch.tensor(q), torch.tensor(k), torch.tensor(v), attn_mask=mask,
+            scale=scale, enable_gqa=True).numpy()
+        assert np.max(np.abs(o - ot)) < 1e-12, (n, np.max(np.abs(o - ot)))
+
+
+def pin_row_sums_and_mask():
+    """Weights sum to 1; masked weights are exactly 0; a -1e9 fill gives the same
+    weights as -inf ([Scratch] 三.2, [Breakdown] section 5 uses -1e9)."""
+    r = _rng(3)
+    q = r.standard_normal((9, 16))
+    k = r.standard_normal((12, 16))
+    qp = np.arange(9) + 3
+    kp = np.arange(12)
+    s, p = oa.scores_and_weights(q, k, scale=0.25, causal=True, q_pos=qp, k_pos=kp)
+    assert np.max(np.abs(p.sum(-1) - 1)) < 1e-15
+    masked = kp[None, :] > qp[:, None]
+    assert masked.any() and np.all(p[masked] == 0.0)
+    assert np.all(p[~masked] > 0)
+    s9 = np.where(masked, -1e9, s)
+    assert np.max(np.abs(oa.softmax(s9) - p)) == 0.0
+
+
+def pin_causal_row0():
+    """Causal query 0 sees only key 0: O_0 = V_0 and lse_0 = S_00, also with RoPE
+    (position 0 is the identity rotation) ([Evolution] section 5 mask)."""
+    for base in (0.0, 10000.0):
+        q, k, v = _rand_inputs(7, 1, 2, 1, 10, 10, 8, "bf16")
+        o, lse = oa.attention(q, k, v, causal=True, scale=0.3, rope_base=base, dtype="bf16")
+        assert np.all(o[0, :, 0] == v[0, 0, 0])
+        s00 = 0.3 * np.dot(q[0, :, 0], k[0, 0, 0].T)
+        assert np.max(np.abs(lse[0, :, 0] - s00)) < 1e-14
+
+
+def pin_uniform_scores():
+    """Q = 0 makes every visible score equal: O_i is the mean of the visible V
+    rows and lse_i = ln(number visible) (closed form of the definition)."""
+    B, Hq, Hkv, Nq, Nk, d = 1, 4, 2, 6, 11, 8
+    _, k, v = _rand_inputs(8, B, Hq, Hkv, Nq, Nk, d, "f64")
+    q = np.zeros((B, Hq, Nq, d))
+    for causal in (False, True):
+        o, lse = oa.attention(q, k, v, causal=causal, scale=0.5, rope_base=0.0, dtype="f64")
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            for i in range(Nq):
+                n = (Nk - Nq + i + 1) if causal else Nk
+                assert np.max(np.abs(o[0, h, i] - v[0, g, :n].mean(0))) < 1e-14
+                assert abs(lse[0, h, i] - math.log(n)) < 1e-14
+
+
+def pin_convex_hull():
+    """Each output row is a convex combination of the visible V rows
+    ([Deconstructed], multi-head section)."""
+    q, k, v = _rand_inputs(9, 1, 2, 2, 16, 16, 8, "f64", sigma=3.0)
+    o, _ = oa.attention(q, k, v, causal=True, scale=0.35, dtype="f64")
+    for h in range(2):
+        for i in range(16):
+            vis = v[0, h, :i + 1]
+            assert np.all(o[0, h, i] >= vis.min(0) - 1e-14)
+            assert np.all(o[0, h, i] <= vis.max(0) + 1e-14)
+
+
+def pin_gqa_equals_mha_repeat():
+    """GQA equals MHA on K/V heads repeated H/H_kv times each, bitwise; H_kv = 1
+    is MQA ([Scratch] 三.4, [Evolution] sections 8-9)."""
+    for Hkv in (1, 2, 4):
+        q, k, v = _rand_inputs(10 + Hkv, 2, 8, Hkv, 7, 9, 8, "bf16")
+        o, lse = oa.attention(q, k, v, causal=True, scale=0.3, rope_base=500.0, dtype="bf16")
+        kr = np.repeat(k, 8 // Hkv, axis=1)
+        vr = np.repeat(v, 8 // Hkv, axis=1)
+        o2, lse2 = oa.attention(q, kr, vr, causal=True, scale=0.3, rope_base=500.0, dtype="bf16")
+        assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+
+
+def pin_rope_relative():
+    """Unrounded RoPE scores depend only on the position difference: q at t and k
+    at t + 2 give the same product for t = 0, 3, 6 ([Scratch] 三.5), q at 3 with k
+    at 7 equals q at 0 with k at 4 ([Breakdown] Key Topic 4); norms are kept."""
+    r = _rng(11)
+    d = 16
+    q = r.standard_normal(d)
+    k = r.standard_normal(d)
+    dots = [np.dot(oa.rope(q[None], [t], 10000.0, "f64")[0],
+                   oa.rope(k[None], [t + 2], 10000.0, "f64")[0]) for t in (0, 3, 6)]
+    assert max(dots) - min(dots) < 1e-12
+    a = np.dot(oa.rope(q[None], [3], 10000.0, "f64")[0], oa.rope(k[None], [7], 10000.0, "f64")[0])
+    b = np.dot(q, oa.rope(k[None], [4], 10000.0, "f64")[0])
+    assert abs(a - b) < 1e-12
+    for p in (1, 17, 1000):
+        x = oa.rope(q[None], [p], 10000.0, "f64")[0]
+        assert abs(np.linalg.norm(x) - np.linalg.norm(q)) < 1e-12
+
+
+def pin_rope_closed_form():
+    """Pair 0 has theta_0 = 1, so (1, 0) at position p becomes (cos p, sin p) and
+    (0, 1) becomes (-sin p, cos p): the counter-clockwise rotation matrix of
+    [Breakdown] section 3.1.  Pair 1 of d = 4 turns by p / sqrt(base)."""
+    for p in (0, 1, 2, 5, 1000):
+        a = oa.rope(np.array([[1.0, 0.0, 1.0, 0.0]]), [p], 400.0, "f64")[0]
+        b = oa.rope(np.array([[0.0, 1.0, 0.0, 1.0]]), [p], 400.0, "f64")[0]
+        t1 = p / 20.0
+        assert np.max(np.abs(a - [math.cos(p), math.sin(p), math.cos(t1), math.sin(t1)])) < 1e-13
+        assert np.max(np.abs(b - [-math.sin(p), math.cos(p), -math.sin(t1), math.cos(t1)])) < 1e-13
+
+
+def pin_rounding_vs_torch():
+    """The rounding model equals torch's fp64 -> fp32 -> bf16 conversions,
+    including values exactly halfway between two bf16 numbers."""
+    r = _rng(12)
+    x = np.concatenate([r.standard_normal(5000) * 10, r.standard_normal(100) * 1e-30])
+    # halfway cases: bf16 grid point + half an ulp, odd and even neighbours
+    base = _bf16_via_torch(r.standard_normal(200))
+    ulp = np.abs(base) * 2.0 ** -7
+    x = np.concatenate([x, base + ulp / 2, base - ulp / 2])
+    assert np.array_equal(oa.round_to_dtype(x, "bf16"), _bf16_via_torch(x))
+    assert np.array_equal(oa.round_to_dtype(x, "f32"), x.astype(np.float32).astype(np.float64))
+    rot = oa.rope(r.standard_normal((4, 8)), np.arange(4), 10000.0, "bf16")
+    assert np.array_equal(rot, _bf16_via_torch(rot))
+
+
+def pin_decode_equals_last_causal_row():
+    """A decode step over a cache of n keys equals row n-1 of causal prefill
+    ([Scratch] 三.6 checks token-by-token decode against full causal attention)."""
+    B, Hq, Hkv, N, d = 2, 4, 2, 13, 8
+    q, k, v = _rand_inputs(13, B, Hq, Hkv, N, N, d, "f64")
+    o, lse = oa.attention(q, k, v, causal=True, scale=0.4, dtype="f64")
+    for n in (1, 5, 13):
+        pad = np.full((B, Hkv, 20, d), np.nan)
+        kc, vc = pad.copy(), pad.copy()
+        kc[:, :, :n] = k[:, :, :n]
+        vc[:, :, :n] = v[:, :, :n]
+        od, ld = oa.decode(q[:, :, n - 1], kc, vc, np.array([n, n]), scale=0.4)
+        # row n-1 of a causal prefill over the first n keys
+        o2, l2 = oa.attention(q[:, :, :n], k[:, :, :n], v[:, :, :n], causal=True,
+                              scale=0.4, dtype="f64")
+        assert np.max(np.abs(od - o2[:, :, n - 1])) < 1e-14
+        assert np.max(np.abs(ld - l2[:, :, n - 1])) < 1e-14
+    assert np.max(np.abs(oa.decode(q[:, :, N - 1], k, v, np.array([N, N]), scale=0.4)[0]
+                         - o[:, :, N - 1])) < 1e-14
+    od, ld = oa.decode(q[:, :, 0], k, v, np.array([0, N]), scale=0.4)
+    assert np.all(od[0] == 0) and np.all(np.isneginf(ld[0]))
+
+
+def pin_score_std():
+    """Unscaled q.k at d = 128 has std ~ 11.3 and 1 after the 1/sqrt(d) scale;
+    with component variance sigma^2 the variance is d sigma^4 ([Breakdown]
+    section 1.2, Key Topic 1)."""
+    g = _golden("score_std.txt")
+    d = int(g["d"][0])
+    r = _rng(14)
+    q = r.standard_normal((512, d))
+    k = r.standard_normal((512, d))
+    pos = np.arange(512)
+    s1, _ = oa.scores_and_weights(q, k, scale=1.0, causal=False, q_pos=pos, k_pos=pos)
+    s2, _ = oa.scores_and_weights(q, k, scale=1.0 / math.sqrt(d), causal=False, q_pos=pos, k_pos=pos)
+    assert abs(np.std(s1) - float(g["unscaled_std"][0])) < 0.15, np.std(s1)
+    assert abs(np.std(s2) - float(g["scaled_std"][0])) < 0.02, np.std(s2)
+    s3, _ = oa.scores_and_weights(4 * q, 4 * k, scale=1.0 / math.sqrt(d), causal=False,
+                                  q_pos=pos, k_pos=pos)
+    assert abs(np.std(s3) - 16.0) < 0.3
+
+
+def pin_lse_identity():
+    """sum_j exp(S_ij - lse_i) over visible keys is 1 ([Scratch] 三.1: log-softmax
+    is x minus logsumexp, and its exponentials sum to one)."""
+    q, k, v = _rand_inputs(15, 1, 2, 1, 10, 14, 8, "f64", sigma=2.0)
+    o, lse = oa.attention(q, k, v, causal=True, scale=0.5, dtype="f64")
+    for h in range(2):
+        s = 0.5 * q[0, h] @ k[0, 0].T
+        vis = np.arange(14)[None, :] <= (np.arange(10) + 4)[:, None]
+        tot = np.where(vis, np.exp(s - lse[0, h][:, None]), 0.0).sum(-1)
+        assert np.max(np.abs(tot - 1)) < 1e-13
+
+
+ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

@@ -1,0 +1,139 @@
+"""Plant plausible mistakes in a copy of the oracle and check that a pin fails.
+
+Each mutation swaps one oracle function for a broken version (dropped scale,
+wrong rotation sign, wrong pairing, wrong head mapping, mask off by one, ...).
+If every pin still passed, the pins would not be able to tell the oracle from
+that mistake.  All of this runs on the CPU against the oracle only.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle.dense as oa
+from oracle_pins import ALL_PINS
+
+_orig_scores = oa.scores_and_weights
+_orig_rope = oa.rope
+_orig_lse = oa.logsumexp
+
+
+def _scores_no_scale(q_rows, k, *, scale, causal, q_pos, k_pos):
+    return _orig_scores(q_rows, k, scale=1.0, causal=causal, q_pos=q_pos, k_pos=k_pos)
+
+
+def _scores_strict(q_rows, k, *, scale, causal, q_pos, k_pos):
+    # mask off by one: j < i instead of j <= i (the diagonal hidden)
+    s = (np.asarray(q_rows) @ np.asarray(k).T) * scale
+    if causal:
+        vis = np.asarray(k_pos)[None, :] < np.asarray(q_pos)[:, None]
+        s = np.where(vis, s, -np.inf)
+    with np.errstate(invalid="ignore"):
+        return s, oa.softmax(s)
+
+
+def _scores_top_left(q_rows, k, *, scale, causal, q_pos, k_pos):
+    # causal aligned at the top-left corner instead of the bottom-right
+    q_pos = np.asarray(q_pos) - (np.asarray(q_pos).min() if len(q_pos) else 0)
+    return _orig_scores(q_rows, k, scale=scale, causal=causal, q_pos=q_pos, k_pos=k_pos)
+
+
+def _scores_transposed(q_rows, k, *, scale, causal, q_pos, k_pos):
+    s = (np.asarray(q_rows) @ np.asarray(k).T) * scale
+    if s.shape[0] == s.shape[1]:
+        s = s.T.copy()
+    if causal:
+        vis = np.asarray(k_pos)[None, :] <= np.asarray(q_pos)[:, None]
+        s = np.where(vis, s, -np.inf)
+    return s, oa.softmax(s)
+
+
+def _rope_neg(x, positions, base, dtype):
+    return _orig_rope(x, -np.asarray(positions), base, dtype) if False else \
+        _rope_generic(x, positions, base, dtype, sign=-1)
+
+
+def _rope_generic(x, positions, base, dtype, sign=1, half=False, expo=2.0):
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    pos = np.asarray(positions, np.float64)
+    th = np.array([math.pow(base, -expo * j / d) for j in range(d // 2)])
+    a = sign * pos[:, None] * th[None, :]
+    c, s = np.cos(a), np.sin(a)
+    if half:
+        x0, x1 = x[..., : d // 2], x[..., d // 2:]
+    else:
+        x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    r0, r1 = x0 * c - x1 * s, x0 * s + x1 * c
+    if half:
+        out[..., : d // 2], out[..., d // 2:] = r0, r1
+    else:
+        out[..., 0::2], out[..., 1::2] = r0, r1
+    return oa.round_to_dtype(out, dtype)
+
+
+def _rope_half(x, positions, base, dtype):
+    return _rope_generic(x, positions, base, dtype, half=True)
+
+
+def _rope_theta(x, positions, base, dtype):
+    return _rope_generic(x, positions, base, dtype, expo=1.0)
+
+
+def _rope_unrounded(x, positions, base, dtype):
+    return _orig_rope(x, positions, base, "f64")
+
+
+def _lse_no_max(x):
+    x = np.asarray(x, np.float64)
+    m = np.max(x, axis=-1, keepdims=True)
+    return np.log(np.sum(np.exp(x - m), axis=-1))
+
+
+def _lse_log2(x):
+    return _orig_lse(x) / math.log(2.0)
+
+
+def _kv_mod(h, Hq, Hkv):
+    return h % Hkv
+
+
+def _round_truncate(x, dtype):
+    x = np.asarray(x, np.float64)
+    if dtype != "bf16":
+        return x.astype(np.float32).astype(np.float64) if dtype == "f32" else x.copy()
+    u = x.astype(np.float32).view(np.uint32) & np.uint32(0xFFFF0000)
+    return u.view(np.float32).astype(np.float64)
+
+
+MUTATIONS = {
+    "dropped_scale": ("scores_and_weights", _scores_no_scale),
+    "mask_off_by_one": ("scores_and_weights", _scores_strict),
+    "causal_top_left": ("scores_and_weights", _scores_top_left),
+    "transposed_scores": ("scores_and_weights", _scores_transposed),
+    "rope_wrong_sign": ("rope", _rope_neg),
+    "rope_rotate_half": ("rope", _rope_half),
+    "rope_wrong_theta": ("rope", _rope_theta),
+    "rope_not_rounded": ("rope", _rope_unrounded),
+    "lse_dropped_max": ("logsumexp", _lse_no_max),
+    "lse_log2": ("logsumexp", _lse_log2),
+    "gqa_mod_mapping": ("_kv_head", _kv_mod),
+    "bf16_truncation": ("round_to_dtype", _round_truncate),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_some_pin_catches(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(oa, attr, fn)
+    oa._COS_SIN_CACHE.clear()
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin detects the mutation {name}"
