@@ -1,0 +1,229 @@
+"""Benchmark: exact attention forward (TFLOP/s) and decode (HBM GB/s) on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  * prefill: causal GQA with RoPE, B=2, Hq=32, Hkv=8, N=8192, d=128, bf16
+    (K rotation pass + tiled attention kernel), and
+  * decode: GQA, B=32, Hq=32, Hkv=8, d=128, bf16 cache, KV lengths ~ U[1024, 32768]
+    (split kernel + merge kernel).
+Inputs are resident in device memory before timing starts.  Each call is
+bracketed by HIP events on the stream it runs on; the step time is the wall
+time of the timed steps between two device synchronisations.
+
+Printed: one JSON line.  ``value`` is the prefill TFLOP/s (algorithmic FLOPs:
+4 * d per visible (query, key) pair per query head), ``decode.value`` the decode
+GB/s (algorithmic bytes: every valid cached K/V row once, plus q, o, lse, lens).
+``roofline`` is for the prefill attention call (MFMA-bound, bf16 dense peak
+2516.6 TFLOP/s), ``decode.roofline`` for the decode call (HBM-bound, 8 TB/s).
+``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
+workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+METRIC = "attn fwd TFLOP/s (causal GQA N=8192 d=128 bf16) + decode HBM GB/s"
+
+
+def visible_pairs(Nq, Nk, causal):
+    if not causal:
+        return Nq * Nk
+    off = Nk - Nq
+    # query i sees keys 0..off+i
+    return Nq * (off + 1) + Nq * (Nq - 1) // 2
+
+
+def fwd_flops(w):
+    return 4.0 * w.d * visible_pairs(w.Nq, w.Nk, w.causal) * w.B * w.Hq
+
+
+def decode_bytes(w, lens):
+    kv = int(np.sum(lens.astype(np.int64))) * w.Hkv * w.d * 2 * 2
+    q = w.B * w.Hq * w.d * 2
+    o = w.B * w.Hq * w.d * 4
+    lse = w.B * w.Hq * 4
+    return kv + q + o + lse + w.B * 4
+
+
+def dev(x):
+    import torch
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(x).cuda()
+
+
+def cpu_baseline(w3, w4, budget_s=12.0):
+    """Time the fp64 oracle on bounded samples of both workloads on the host."""
+    import oracle.dense as oa
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    # prefill sample: rows of head (0, 0), spread over the sequence
+    q, k, v = W.fwd_inputs(w3, B=1, Hq=1, Hkv=1)
+    rows_all = np.random.default_rng(0).permutation(w3.Nq)
+    t0 = time.perf_counter()
+    done = 0
+    pairs = 0
+    kc = {}
+    while time.perf_counter() - t0 < budget_s * 0.5 and done < w3.Nq:
+        rows = np.sort(rows_all[done:done + 256])
+        oa.attention_rows(q, k, v, 0, 0, rows, causal=True, scale=w3.scale,
+                          rope_base=w3.rope_base, dtype="bf16", _kcache=kc)
+        pairs += int(np.sum(rows + (w3.Nk - w3.Nq) + 1))
+        done += len(rows)
+    t_pf = time.perf_counter() - t0
+    tflops = 4.0 * w3.d * pairs / t_pf / 1e12
+    # decode sample: full sequences of the decode workload, one after another
+    lens = W.decode_lens(w4)[:4]
+    qd, kcache, vcache = W.decode_inputs(w4, lens, max_len=int(lens.max()))
+    t0 = time.perf_counter()
+    nb = 0
+    nbytes = 0
+    while time.perf_counter() - t0 < budget_s * 0.5 and nb < len(lens):
+        oa.decode(qd[nb:nb + 1], kcache[nb:nb + 1], vcache[nb:nb + 1], lens[nb:nb + 1], scale=w4.scale)
+        nbytes += int(lens[nb]) * w4.Hkv * w4.d * 2 * 2
+        nb += 1
+    t_dec = time.perf_counter() - t0
+    return {
+        "value": tflops, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+        "sample": f"prefill: {done} query rows of head (0,0) of the causal GQA N=8192 workload "
+                  f"({t_pf:.1f} s, fp64 NumPy, RoPE + dense score rows); decode: {nb} full "
+                  f"sequences of the decode workload ({t_dec:.1f} s)",
+        "decode_value": nbytes / t_dec / 1e9, "decode_unit": "GB/s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="time one leg only (for profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_scaled_dot_amd as esd
+
+    w3 = W.WORKLOADS["c3"]
+    w4 = W.WORKLOADS["c4"]
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    print("[bench] generating inputs", file=sys.stderr, flush=True)
+    q, k, v = W.fwd_inputs(w3)
+    dq, dk, dv = dev(q), dev(k), dev(v)
+    del q, k, v
+    o3 = torch.empty((w3.B, w3.Hq, w3.Nq, w3.d), dtype=torch.float32, device="cuda")
+    l3 = torch.empty((w3.B, w3.Hq, w3.Nq), dtype=torch.float32, device="cuda")
+    ws3 = torch.empty(esd.fwd_workspace_bytes(w3.B, w3.Hkv, w3.Nk, w3.d, w3.rope_base, esd.ATTN_BF16),
+                      dtype=torch.uint8, device="cuda")
+    lens = W.decode_lens(w4)
+    qd, kc, vc = W.decode_inputs(w4, lens)
+    dqd, dkc, dvc, dlens = dev(qd), dev(kc), dev(vc), dev(lens)
+    del qd, kc, vc
+    o4 = torch.empty((w4.B, w4.Hq, w4.d), dtype=torch.float32, device="cuda")
+    l4 = torch.empty((w4.B, w4.Hq), dtype=torch.float32, device="cuda")
+    ws4 = torch.empty(esd.decode_workspace_bytes(w4.B, w4.Hq, w4.Hkv, w4.max_len, w4.d),
+                      dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    do_pf = args.only in (None, "prefill")
+    do_dec = args.only in (None, "decode")
+
+    def step(evs=None):
+        if do_pf:
+            if evs: evs[0].record(stream)
+            esd.fwd(dq, dk, dv, causal=True, scale=w3.scale, rope_base=w3.rope_base, out=o3, lse=l3,
+                    workspace=ws3)
+            if evs: evs[1].record(stream)
+        if do_dec:
+            if evs: evs[2].record(stream)
+            esd.decode(dqd, dkc, dvc, dlens, scale=w4.scale, out=o4, lse=l4, workspace=ws4)
+            if evs: evs[3].record(stream)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    print("[bench] timing", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pf_ms = [e[0].elapsed_time(e[1]) for e in evs] if do_pf else [float("nan")]
+    dec_ms = [e[2].elapsed_time(e[3]) for e in evs] if do_dec else [float("nan")]
+    pf_avg = float(np.mean(pf_ms))
+    dec_avg = float(np.mean(dec_ms))
+
+    flops = fwd_flops(w3)
+    nbytes = decode_bytes(w4, lens)
+    tflops = flops / (pf_avg * 1e-3) / 1e12 if do_pf else None
+    gbs = nbytes / (dec_avg * 1e-3) / 1e9 if do_dec else None
+
+    rec = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "prefill: causal GQA + RoPE 1e4, B=2 Hq=32 Hkv=8 N=8192 d=128 bf16; "
+                        "decode: GQA B=32 Hq=32 Hkv=8 d=128 bf16, lens ~ U[1024,32768] seed 4004",
+            "prefill_flops": flops, "prefill_ms": pf_avg, "prefill_ms_min": float(np.min(pf_ms)),
+            "decode_bytes": nbytes, "decode_ms": dec_avg, "decode_ms_min": float(np.min(dec_ms)),
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": (tflops / PEAK_BF16_TFLOPS) if tflops else None, "traffic": None,
+        },
+        "decode": {
+            "value": gbs, "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": (gbs / PEAK_HBM_GBS) if gbs else None, "traffic": None},
+        },
+        "context": {
+            "a100_roofline": "312 TFLOPS FP16, 1555 GB/s, ~200 FLOP/B",
+            "materialised_scores_fp16_n8192_per_head_MB": 8192 * 8192 * 2 / 2 ** 20,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w3, w4)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

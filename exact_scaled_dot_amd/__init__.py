@@ -1,0 +1,180 @@
+"""Exact scaled-dot-product attention for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over ``libattn.so`` (C ABI declared in ``include/attn.h``).
+This module only marshals arguments: shapes, dtypes and pointers of torch
+device tensors go to the library, which validates them and runs every step on
+the GPU.  torch provides device memory and the current stream.  There is no
+fallback: if the library is missing, every call raises.
+
+Functions (same names as the C entry points):
+  fwd(q, k, v, causal, scale=None, rope_base=0.0, out=None, lse=None, workspace=None)
+  decode(q, k_cache, v_cache, seq_lens, scale=None, out=None, lse=None, workspace=None)
+  rope_apply(x, rope_base, pos_offset=0, out=None)
+  fwd_workspace_bytes(...), decode_workspace_bytes(...), status_str(code)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_BF16 = 0
+ATTN_F32 = 1
+STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_HIP",
+          4: "ATTN_ERR_WORKSPACE"}
+
+EXPORTS = ("attn_status_str", "attn_fwd_workspace_bytes", "attn_fwd",
+           "attn_decode_workspace_bytes", "attn_decode", "attn_rope_apply")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn, code):
+        self.code = code
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)}")
+
+
+def lib():
+    """Load libattn.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m exact_scaled_dot_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.attn_status_str.argtypes = [i]
+    L.attn_status_str.restype = ctypes.c_char_p
+    L.attn_fwd_workspace_bytes.argtypes = [i, i, i, i, f, i]
+    L.attn_fwd_workspace_bytes.restype = sz
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, f, i, vp, sz, vp]
+    L.attn_fwd.restype = i
+    L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.attn_decode_workspace_bytes.restype = sz
+    L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    L.attn_decode.restype = i
+    L.attn_rope_apply.argtypes = [vp, vp, i, i, i, i, i, f, i, vp]
+    L.attn_rope_apply.restype = i
+    _lib = L
+    return L
+
+
+def status_str(code: int) -> str:
+    return lib().attn_status_str(int(code)).decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(fn, code):
+    if code != 0:
+        raise AttnError(fn, code)
+
+
+def _need_cuda_contig(name, t):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def fwd_workspace_bytes(B, Hkv, Nk, d, rope_base, dtype_code) -> int:
+    return int(lib().attn_fwd_workspace_bytes(B, Hkv, Nk, d, float(rope_base), dtype_code))
+
+
+def decode_workspace_bytes(B, Hq, Hkv, max_len, d) -> int:
+    return int(lib().attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d))
+
+
+def fwd(q, k, v, causal: bool, scale=None, rope_base: float = 0.0, out=None, lse=None,
+        workspace=None, want_lse: bool = True):
+    """O [B,Hq,Nq,d] fp32 and lse [B,Hq,Nq] fp32 of softmax(scale QK^T + M) V."""
+    import torch
+    L = lib()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _need_cuda_contig(n, t)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if (Bk, dk) != (B, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch between q, k and v")
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, Nq, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    need = fwd_workspace_bytes(B, Hkv, Nk, d, rope_base, code)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("attn_fwd", L.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv,
+                                  Nq, Nk, d, int(bool(causal)), float(scale), float(rope_base),
+                                  code, _ptr(workspace), wsb, _stream()))
+    return out, lse
+
+
+def decode(q, k_cache, v_cache, seq_lens, scale=None, out=None, lse=None, workspace=None,
+           want_lse: bool = True):
+    """One-query attention per sequence over cache rows 0..seq_lens[b]-1."""
+    import torch
+    L = lib()
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
+        _need_cuda_contig(n, t)
+    if seq_lens.dtype != torch.int32:
+        raise TypeError("seq_lens must be int32")
+    B, Hq, d = q.shape
+    Bc, Hkv, max_len, dc = k_cache.shape
+    if (Bc, dc) != (B, d) or tuple(v_cache.shape) != tuple(k_cache.shape) or seq_lens.numel() != B:
+        raise ValueError("shape mismatch between q, caches and seq_lens")
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, Hq, Hkv, max_len, d)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("attn_decode", L.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                        _ptr(out), _ptr(lse), B, Hq, Hkv, max_len, d,
+                                        float(scale), code, _ptr(workspace), wsb, _stream()))
+    return out, lse
+
+
+def rope_apply(x, rope_base: float, pos_offset: int = 0, out=None):
+    """RoPE of x [B,H,N,d] at positions pos_offset + n, rounded to x's dtype."""
+    import torch
+    L = lib()
+    _need_cuda_contig("x", x)
+    B, H, N, d = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _check("attn_rope_apply", L.attn_rope_apply(_ptr(x), _ptr(out), B, H, N, d, int(pos_offset),
+                                                float(rope_base), _dtype_code(x), _stream()))
+    return out

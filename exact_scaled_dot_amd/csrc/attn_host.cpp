@@ -1,0 +1,190 @@
+// C ABI of libattn: argument validation, workspace sizing and dispatch.
+//
+// Every argument is checked on the host before the first HIP call, so invalid
+// input never reaches a kernel.  Status codes are returned; nothing throws.
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/attn.h"
+#include "launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_d(int d) { return d == 64 || d == 128; }
+
+size_t elem_size(attn_dtype t) { return t == ATTN_F32 ? 4 : 2; }
+
+bool known_dtype(int t) { return t == ATTN_BF16 || t == ATTN_F32; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+bool log_enabled() {
+    static int on = -1;
+    if (on < 0) {
+        const char* s = std::getenv("ATTN_LOG");
+        on = (s && s[0] == '1') ? 1 : 0;
+    }
+    return on == 1;
+}
+
+int fail(int code, const char* what) {
+    if (log_enabled()) fprintf(stderr, "[attn] %s: %s\n", attn_status_str(code), what);
+    return code;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_str(int status) {
+    switch (status) {
+        case ATTN_OK: return "ATTN_OK";
+        case ATTN_ERR_INVALID: return "ATTN_ERR_INVALID";
+        case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+        case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+        case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
+        default: return "ATTN_ERR_UNKNOWN";
+    }
+}
+
+size_t attn_fwd_workspace_bytes(int B, int Hkv, int Nk, int d, float rope_base, attn_dtype dtype) {
+    if (!(rope_base > 0.f) || B <= 0 || Hkv <= 0 || Nk <= 0 || d <= 0 || !known_dtype(dtype))
+        return 0;
+    return (size_t)B * Hkv * Nk * d * elem_size(dtype);
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
+             int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+             float scale, float rope_base, attn_dtype dtype,
+             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (B < 0 || Hq < 0 || Nq < 0) return fail(ATTN_ERR_INVALID, "negative size");
+    if (Hkv < 1 || Nk < 1 || d < 1) return fail(ATTN_ERR_INVALID, "Hkv, Nk and d must be >= 1");
+    if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID, "Hq must be a multiple of Hkv");
+    if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID, "causal must be 0 or 1");
+    if (causal && Nq > Nk) return fail(ATTN_ERR_INVALID, "causal needs Nq <= Nk");
+    if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID, "scale must be finite");
+    if (rope_base != 0.f && !(std::isfinite(rope_base) && rope_base > 0.f))
+        return fail(ATTN_ERR_INVALID, "rope_base must be 0 or a finite positive base");
+    if (!known_dtype(dtype)) return fail(ATTN_ERR_INVALID, "unknown dtype");
+    if (!supported_d(d)) return fail(ATTN_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+    if (B == 0 || Hq == 0 || Nq == 0) return ATTN_OK;
+    if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID, "null pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(ATTN_ERR_INVALID, "q, k, v, o must be 16-byte aligned");
+    const bool rope = rope_base > 0.f;
+    const size_t need = attn_fwd_workspace_bytes(B, Hkv, Nk, d, rope_base, dtype);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return fail(ATTN_ERR_WORKSPACE, "workspace missing or too small for the rotated K");
+    if (need > 0 && !aligned16(workspace)) return fail(ATTN_ERR_INVALID, "workspace must be 16-byte aligned");
+
+    attn::FwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.d = d;
+    a.causal = causal; a.scale = scale; a.rope_tab = nullptr;
+
+    if (rope) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return fail(ATTN_ERR_HIP, "hipGetDevice");
+        const double2* tab = attn::rope_table(dev, rope_base, d, Nk, &e);
+        if (!tab) return fail(ATTN_ERR_HIP, "RoPE table");
+        // K rotated once into the workspace; Q is rotated as it is loaded.
+        const long long rows = (long long)B * Hkv * Nk;
+        if (dtype == ATTN_BF16)
+            e = attn::launch_rope_bf16(static_cast<const uint16_t*>(k), static_cast<uint16_t*>(workspace),
+                                       rows, Nk, d, 0, tab, stream);
+        else
+            e = attn::launch_rope_f32(static_cast<const float*>(k), static_cast<float*>(workspace),
+                                      rows, Nk, d, 0, tab, stream);
+        if (e != hipSuccess) return fail(ATTN_ERR_HIP, "rope launch");
+        a.k = workspace;
+        a.rope_tab = tab;
+    }
+    hipError_t e = dtype == ATTN_BF16 ? attn::launch_prefill_bf16(a, stream)
+                                      : attn::launch_prefill_f32(a, stream);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, hipGetErrorString(e));
+    return ATTN_OK;
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int d) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_len <= 0 || d <= 0) return 0;
+    const size_t nch = (size_t)(max_len + attn::kDecodeChunk - 1) / attn::kDecodeChunk;
+    const size_t rows = (size_t)B * Hq * nch;
+    size_t o_bytes = rows * d * sizeof(float);
+    o_bytes = (o_bytes + 255) & ~(size_t)255;
+    return o_bytes + rows * sizeof(float);
+}
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* seq_lens, float* o, float* lse,
+                int B, int Hq, int Hkv, int max_len, int d, float scale,
+                attn_dtype dtype, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+    if (B < 0 || Hq < 0) return fail(ATTN_ERR_INVALID, "negative size");
+    if (Hkv < 1 || max_len < 1 || d < 1) return fail(ATTN_ERR_INVALID, "Hkv, max_len and d must be >= 1");
+    if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID, "Hq must be a multiple of Hkv");
+    if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID, "scale must be finite");
+    if (!known_dtype(dtype)) return fail(ATTN_ERR_INVALID, "unknown dtype");
+    if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode is built for bf16");
+    if (!supported_d(d)) return fail(ATTN_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+    if (B == 0 || Hq == 0) return ATTN_OK;
+    if (!q || !k_cache || !v_cache || !seq_lens || !o) return fail(ATTN_ERR_INVALID, "null pointer");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+        return fail(ATTN_ERR_INVALID, "q, caches and o must be 16-byte aligned");
+    const size_t need = attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "decode workspace missing or too small");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(ATTN_ERR_INVALID, "decode workspace must be 256-byte aligned");
+
+    attn::DecodeArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k_cache);
+    a.v = static_cast<const uint16_t*>(v_cache);
+    a.lens = seq_lens;
+    a.o = o; a.lse = lse;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.max_len = max_len; a.d = d; a.scale = scale;
+    a.nchunks = (max_len + attn::kDecodeChunk - 1) / attn::kDecodeChunk;
+    const size_t rows = (size_t)B * Hq * a.nchunks;
+    size_t o_bytes = (rows * d * sizeof(float) + 255) & ~(size_t)255;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+    hipError_t e = attn::launch_decode_bf16(a, stream);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, hipGetErrorString(e));
+    return ATTN_OK;
+}
+
+int attn_rope_apply(const void* x, void* out, int B, int H, int N, int d,
+                    int pos_offset, float rope_base, attn_dtype dtype,
+                    hipStream_t stream) {
+    if (B < 0 || H < 0 || N < 0 || pos_offset < 0) return fail(ATTN_ERR_INVALID, "negative size");
+    if (d < 2 || d % 2) return fail(ATTN_ERR_INVALID, "RoPE needs an even head dim");
+    if (!(std::isfinite(rope_base) && rope_base > 0.f)) return fail(ATTN_ERR_INVALID, "rope_base must be finite and > 0");
+    if (!known_dtype(dtype)) return fail(ATTN_ERR_INVALID, "unknown dtype");
+    if (d % (dtype == ATTN_BF16 ? 8 : 4) != 0 || d > 512)
+        return fail(ATTN_ERR_UNSUPPORTED, "head dim must be a multiple of 8 (bf16) / 4 (f32), <= 512");
+    if ((long long)pos_offset + N > 0x40000000LL) return fail(ATTN_ERR_INVALID, "positions too large");
+    if (B == 0 || H == 0 || N == 0) return ATTN_OK;
+    if (!x || !out) return fail(ATTN_ERR_INVALID, "null pointer");
+    if (!aligned16(x) || !aligned16(out)) return fail(ATTN_ERR_INVALID, "x and out must be 16-byte aligned");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "hipGetDevice");
+    const double2* tab = attn::rope_table(dev, rope_base, d, pos_offset + N, &e);
+    if (!tab) return fail(ATTN_ERR_HIP, "RoPE table");
+    const long long rows = (long long)B * H * N;
+    if (dtype == ATTN_BF16)
+        e = attn::launch_rope_bf16(static_cast<const uint16_t*>(x), static_cast<uint16_t*>(out), rows, N, d,
+                                   pos_offset, tab, stream);
+    else
+        e = attn::launch_rope_f32(static_cast<const float*>(x), static_cast<float*>(out), rows, N, d,
+                                  pos_offset, tab, stream);
+    return e == hipSuccess ? ATTN_OK : fail(ATTN_ERR_HIP, hipGetErrorString(e));
+}
+
+}  // extern "C"

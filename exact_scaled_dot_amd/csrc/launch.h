@@ -1,0 +1,54 @@
+// Internal launchers behind the C ABI (host side).  Arguments are validated by
+// the entry points in attn_host.cpp before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdArgs {
+    const void* q;
+    const void* k;  // rotated K when RoPE is on
+    const void* v;
+    float* o;
+    float* lse;
+    int B, Hq, Hkv, Nq, Nk, d;
+    int causal;
+    float scale;
+    const double2* rope_tab;  // null: no RoPE on Q
+};
+
+hipError_t launch_prefill_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_prefill_f32(const FwdArgs& a, hipStream_t stream);
+
+// out[bh, n, :] = rotate(x[bh, n, :], pos_offset + n)
+hipError_t launch_rope_bf16(const uint16_t* x, uint16_t* out, long long rows, int N, int d,
+                            int pos_offset, const double2* tab, hipStream_t stream);
+hipError_t launch_rope_f32(const float* x, float* out, long long rows, int N, int d,
+                           int pos_offset, const double2* tab, hipStream_t stream);
+
+struct DecodeArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* lens;
+    float* o;
+    float* lse;
+    int B, Hq, Hkv, max_len, d;
+    float scale;
+    float* ws_o;    // [B, Hq, nchunks, d]
+    float* ws_lse;  // [B, Hq, nchunks] (log2 domain)
+    int nchunks;
+};
+
+constexpr int kDecodeChunk = 256;  // keys per split workgroup
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+
+// Device table of (cos, sin) in fp64, [npos][d/2]; created or grown on demand.
+// Returns null on failure (HIP error stored in *err).
+const double2* rope_table(int device, float base, int d, int npos, hipError_t* err);
+
+}  // namespace attn

@@ -1,0 +1,134 @@
+/*
+ * attn.h - exact scaled-dot-product attention on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libattn.so.  Every entry point takes plain device pointers, sizes
+ * and a HIP stream, returns an attn_status and never throws.  Work is queued
+ * asynchronously on `stream`; no entry point synchronises the device.
+ *
+ * What is computed (page titles, sections):
+ *   O = softmax(scale * Q K^T + M) V with M = 0 (no mask) or the causal mask
+ *   (minus infinity above the diagonal), per query head, as in
+ *   "Transformer Architecture Breakdown", section 1.2 and Key Topic 5, and
+ *   "Attention mechanisms: from alignment to efficient long context", Notation.
+ *   The score matrix is processed in tiles with the online-softmax recurrence
+ *   (running max, running sum, rescaled accumulator: "Transformer Architecture
+ *   Breakdown", section 4.2; "coding-interview attention from scratch", 三.7),
+ *   so it never reaches device memory.
+ *
+ * Layouts (all contiguous, head dimension fastest, 64-bit offsets inside):
+ *   q   [B, Hq,  Nq, d]      k, v [B, Hkv, Nk, d]     (dtype of the call)
+ *   o   [B, Hq,  Nq, d] fp32 lse  [B, Hq, Nq] fp32 natural-log logsumexp
+ *   Query head h reads KV head h / (Hq / Hkv): MHA (Hkv = Hq), GQA, MQA
+ *   (Hkv = 1) ("coding-interview attention from scratch", 三.4).
+ *
+ * Causal alignment: query i sits at position Nk - Nq + i, key j at j; key j is
+ * visible to query i iff j <= Nk - Nq + i (the bottom-right alignment the
+ * from-scratch page gives for t new tokens over a cache, section 八 question 5).
+ * Causal calls need Nq <= Nk, so no row is fully masked.
+ *
+ * RoPE (rope_base > 0): adjacent pairs (x_2j, x_2j+1) of Q and K rotate by
+ * position * theta_j, theta_j = rope_base^(-2j/d) ("Transformer Architecture
+ * Breakdown", section 3.1; "coding-interview attention from scratch", 三.5);
+ * V is not rotated.  The rotation is evaluated in fp64 (cos/sin from the C
+ * library) and rounded to the input dtype (fp64 -> fp32 -> bf16, nearest-even)
+ * before the product, so the result is the attention of the rounded rotated
+ * operands.
+ *
+ * Ownership: the caller owns every buffer, including workspaces.  The library
+ * keeps one device table of fp64 cos/sin per (device, rope_base, d), created on
+ * the first RoPE call that needs it (a blocking upload) and kept until exit.
+ * Entry points are thread-safe; calls that share a workspace must be ordered by
+ * the caller (same stream or events).
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_BF16 = 0, /* bfloat16 inputs (bits in uint16 storage) */
+    ATTN_F32 = 1   /* float32 inputs */
+} attn_dtype;
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID = 1,     /* bad argument: null pointer, negative size, Hq % Hkv,
+                                 causal with Nq > Nk, non-finite scale, misaligned
+                                 pointer (16 bytes needed) ... */
+    ATTN_ERR_UNSUPPORTED = 2, /* valid but not built: d not in {64, 128}, f32 decode */
+    ATTN_ERR_HIP = 3,         /* a HIP call or kernel launch failed */
+    ATTN_ERR_WORKSPACE = 4    /* workspace missing or smaller than required */
+} attn_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* attn_status_str(int status);
+
+/* Bytes of workspace attn_fwd needs: B*Hkv*Nk*d elements of the input dtype
+ * for the rotated K when rope_base > 0, else 0. */
+size_t attn_fwd_workspace_bytes(int B, int Hkv, int Nk, int d, float rope_base,
+                                attn_dtype dtype);
+
+/*
+ * Prefill / full attention forward.
+ *   q, k, v     device pointers, layouts above, element type `dtype`.
+ *   o           device fp32 [B,Hq,Nq,d], written.
+ *   lse         device fp32 [B,Hq,Nq] or NULL; natural-log logsumexp of each
+ *               row's visible scaled scores.
+ *   B, Hq, Hkv, Nq, Nk, d   sizes; B = 0, Hq = 0 or Nq = 0 is a no-op.
+ *               Hkv >= 1, Hq % Hkv == 0, Nk >= 1, d in {64, 128}.
+ *   causal      0 or 1.
+ *   scale       finite multiplier of Q K^T (1/sqrt(d) for standard attention).
+ *   rope_base   0 = no RoPE, else a finite base > 0.
+ *   workspace   device buffer of attn_fwd_workspace_bytes(...) bytes (may be
+ *               NULL when that is 0); holds the rotated K during the call.
+ * All validation happens on the host before any HIP call.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
+             int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+             float scale, float rope_base, attn_dtype dtype,
+             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace attn_decode needs for partial (max/sum, O) states. */
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int d);
+
+/*
+ * Decode: one query per sequence against a contiguous KV cache, no mask, no
+ * RoPE (cached keys are stored already rotated), as in "coding-interview
+ * attention from scratch", 三.6.  The cache is split along its length; every
+ * chunk yields a partial (max, sum, O) state and a second kernel merges them
+ * exactly ("Transformer Architecture Breakdown", section 4.2 merge rule).
+ *   q          device [B, Hq, d] bf16.
+ *   k_cache, v_cache  device [B, Hkv, max_len, d] bf16; sequence b uses rows
+ *              0 .. seq_lens[b]-1; rows past that are never read.
+ *   seq_lens   device int32 [B]; values are clamped to [0, max_len].  A length
+ *              of 0 yields O = 0 and lse = -inf.
+ *   o          device fp32 [B, Hq, d];  lse  device fp32 [B, Hq] or NULL.
+ *   workspace  device buffer of attn_decode_workspace_bytes(...) bytes.
+ * dtype must be ATTN_BF16 (ATTN_F32 returns ATTN_ERR_UNSUPPORTED).
+ */
+int attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* seq_lens, float* o, float* lse,
+                int B, int Hq, int Hkv, int max_len, int d, float scale,
+                attn_dtype dtype, void* workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/*
+ * RoPE on its own: out[b,h,n,:] = rotate(x[b,h,n,:], position pos_offset + n),
+ * rounded to `dtype` exactly as attn_fwd rounds the rotated operands.
+ * x, out  device [B, H, N, d] of `dtype` (may alias).  d even, d <= 256.
+ */
+int attn_rope_apply(const void* x, void* out, int B, int H, int N, int d,
+                    int pos_offset, float rope_base, attn_dtype dtype,
+                    hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

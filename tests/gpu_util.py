@@ -1,0 +1,48 @@
+"""Helpers for the GPU tests: move seeded numpy inputs to the device and compare."""
+
+import math
+import sys
+
+import numpy as np
+
+
+def dev(x):
+    """numpy uint16 (bf16 bits) / float32 / int32 array -> contiguous cuda tensor."""
+    import torch
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(x).cuda()
+
+
+def host(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def say(*a):
+    print("[gpu-test]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def max_err(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    if a.size == 0:
+        return 0.0
+    return float(np.max(np.abs(a - b)))
+
+
+TOL = {"bf16": (1e-2, 1e-3), "f32": (1e-4, 1e-4)}
+
+
+def check(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what=""):
+    to, tl = TOL[dtype]
+    eo = max_err(o_gpu, o_ref)
+    el = max_err(lse_gpu, lse_ref)
+    say(f"{what}: max|dO|={eo:.3e} (tol {to}), max|dlse|={el:.3e} (tol {tl})")
+    assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(lse_gpu)), what
+    assert eo <= to, (what, eo)
+    assert el <= tl, (what, el)

@@ -1,0 +1,105 @@
+"""The C-ABI library loads, exports what include/attn.h declares, and rejects
+invalid arguments on the host before any HIP call (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_scaled_dot_amd as esd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(esd.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = esd.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    for code, name in esd.STATUS.items():
+        assert esd.status_str(code) == name
+    assert esd.status_str(99) == "ATTN_ERR_UNKNOWN"
+
+
+def test_workspace_sizes():
+    assert esd.fwd_workspace_bytes(2, 8, 8192, 128, 0.0, esd.ATTN_BF16) == 0
+    assert esd.fwd_workspace_bytes(2, 8, 8192, 128, 10000.0, esd.ATTN_BF16) == 2 * 8 * 8192 * 128 * 2
+    assert esd.fwd_workspace_bytes(1, 1, 256, 64, 100.0, esd.ATTN_F32) == 256 * 64 * 4
+    n = esd.decode_workspace_bytes(32, 32, 8, 32768, 128)
+    rows = 32 * 32 * (32768 // 256)
+    assert n >= rows * 129 * 4 and n < rows * 129 * 4 + 256
+    assert esd.decode_workspace_bytes(0, 32, 8, 32768, 128) == 0
+
+
+P = ctypes.c_void_p(256)  # a non-null, aligned, never dereferenced address
+
+
+def _fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Hq=4, Hkv=2, Nq=8, Nk=8, d=64, causal=1,
+             scale=0.125, rope=0.0, dtype=esd.ATTN_BF16, ws=None, wsb=0)
+    a.update(kw)
+    return esd.lib().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                              a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"], a["rope"],
+                              a["dtype"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(B=-1), 1), (dict(Hkv=0), 1),
+    (dict(Hq=6, Hkv=4), 1), (dict(causal=2), 1), (dict(Nq=9, Nk=8), 1),
+    (dict(Nk=0), 1), (dict(scale=float("inf")), 1), (dict(scale=float("nan")), 1),
+    (dict(rope=-1.0), 1), (dict(rope=float("inf")), 1), (dict(dtype=7), 1),
+    (dict(d=96), 2), (dict(d=32), 2), (dict(q=ctypes.c_void_p(258)), 1),
+    (dict(rope=10000.0), 4), (dict(rope=10000.0, ws=P, wsb=100), 4),
+])
+def test_fwd_rejects_on_host(kw, code):
+    assert _fwd(**kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(Hq=0, Hkv=1), dict(Nq=0)])
+def test_fwd_empty_is_a_noop(kw):
+    assert _fwd(q=None, k=None, v=None, o=None, **kw) == 0
+
+
+def _dec(**kw):
+    a = dict(q=P, k=P, v=P, lens=P, o=P, lse=None, B=2, Hq=8, Hkv=2, max_len=64, d=128,
+             scale=0.1, dtype=esd.ATTN_BF16, ws=P, wsb=1 << 20)
+    a.update(kw)
+    return esd.lib().attn_decode(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"], a["B"],
+                                 a["Hq"], a["Hkv"], a["max_len"], a["d"], a["scale"], a["dtype"],
+                                 a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lens=None), 1), (dict(k=None), 1), (dict(Hq=6, Hkv=4), 1), (dict(max_len=0), 1),
+    (dict(scale=float("nan")), 1), (dict(dtype=esd.ATTN_F32), 2), (dict(d=80), 2),
+    (dict(ws=None), 4), (dict(wsb=10), 4), (dict(ws=ctypes.c_void_p(272)), 1),
+])
+def test_decode_rejects_on_host(kw, code):
+    assert _dec(**kw) == code
+
+
+def test_decode_empty_is_a_noop():
+    assert _dec(B=0, q=None, k=None, v=None, lens=None, o=None, ws=None, wsb=0) == 0
+
+
+def test_rope_apply_rejects_on_host():
+    L = esd.lib()
+    assert L.attn_rope_apply(P, P, 1, 1, 4, 7, 0, 100.0, esd.ATTN_BF16, None) == 1
+    assert L.attn_rope_apply(P, P, 1, 1, 4, 12, 0, 100.0, esd.ATTN_BF16, None) == 2
+    assert L.attn_rope_apply(P, P, 1, 1, 4, 16, 0, 0.0, esd.ATTN_BF16, None) == 1
+    assert L.attn_rope_apply(None, P, 1, 1, 4, 16, 0, 100.0, esd.ATTN_BF16, None) == 1
+    assert L.attn_rope_apply(None, None, 0, 1, 4, 16, 0, 100.0, esd.ATTN_BF16, None) == 0
