@@ -67,7 +67,7 @@ int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
     if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID, "Hq must be a multiple of Hkv");
     if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID, "causal must be 0 or 1");
     if (causal && Nq > Nk) return fail(ATTN_ERR_INVALID, "causal needs Nq <= Nk");
-    if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID, "scale must be finite");
+    if (!(std::isfinite(scale) && scale > 0.f)) return fail(ATTN_ERR_INVALID, "scale must be finite and > 0");
     if (rope_base != 0.f && !(std::isfinite(rope_base) && rope_base > 0.f))
         return fail(ATTN_ERR_INVALID, "rope_base must be 0 or a finite positive base");
     if (!known_dtype(dtype)) return fail(ATTN_ERR_INVALID, "unknown dtype");
@@ -128,7 +128,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
     if (B < 0 || Hq < 0) return fail(ATTN_ERR_INVALID, "negative size");
     if (Hkv < 1 || max_len < 1 || d < 1) return fail(ATTN_ERR_INVALID, "Hkv, max_len and d must be >= 1");
     if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID, "Hq must be a multiple of Hkv");
-    if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID, "scale must be finite");
+    if (!(std::isfinite(scale) && scale > 0.f)) return fail(ATTN_ERR_INVALID, "scale must be finite and > 0");
     if (!known_dtype(dtype)) return fail(ATTN_ERR_INVALID, "unknown dtype");
     if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode is built for bf16");
     if (!supported_d(d)) return fail(ATTN_ERR_UNSUPPORTED, "head dim must be 64 or 128");

@@ -16,9 +16,9 @@
 // gfx950 mapping of the split kernel (256 keys, one KV head, GP query heads):
 //   * S = K q^T on v_mfma_f32_16x16x32_bf16: A = 16 cached keys, B = the query
 //     heads of the group (columns), so every K row is read from memory once and
-//     serves all heads that share it.  A lane loads 64 contiguous bytes of one
-//     key row (the d-slots of the MFMA are permuted to match), so a wave's
-//     load covers 16 whole rows = 4 KB.
+//     serves all heads that share it.  For MFMA step s the four lanes that hold
+//     one key read its d range [32s, 32s + 32) (64 contiguous bytes); the same
+//     d-slot order is used for q, so the dot products are unchanged.
 //   * P V on the vector ALU: V rows stream in 16-byte pieces, weights come from
 //     LDS as broadcasts; partial sums are reduced across lanes, then waves.
 
@@ -39,7 +39,6 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     float* __restrict__ ws_o, float* __restrict__ ws_lse, int B, int Hq,
                     int Hkv, int max_len, float scale_log2, int nchunks, int nhch) {
     static_assert(D == 64 || D == 128, "head dim");
-    constexpr int DQ = D / 4;           // d-range per lane quarter in the QK MFMA
     constexpr int NS = D / 32;          // MFMA k-steps over d
     constexpr int NDC = D / 8;          // 16-byte pieces per row
     constexpr int NKS = 64 / NDC;       // key slots per wave in the PV loop
@@ -83,7 +82,7 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             uint4 x = make_uint4(0, 0, 0, 0);
-            if (key < len) x = *reinterpret_cast<const uint4*>(kb + (size_t)key * D + DQ * quarter + 8 * s);
+            if (key < len) x = *reinterpret_cast<const uint4*>(kb + (size_t)key * D + 32 * s + 8 * quarter);
             kf[grp][s] = x;
         }
     }
@@ -98,7 +97,7 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         vf[it] = x;
     }
 
-    // ---- q operand: column r16 = head, k-slots 8*quarter.. = d DQ*quarter + 8s ..
+    // ---- q operand: column r16 = head, k-slots 8*quarter.. = d 32s + 8*quarter ..
     bf16x8 qf[NS];
     {
         const bool ok = r16 < nh;
@@ -106,7 +105,7 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             uint4 x = make_uint4(0, 0, 0, 0);
-            if (ok) x = *reinterpret_cast<const uint4*>(qrow + DQ * quarter + 8 * s);
+            if (ok) x = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * quarter);
             qf[s] = __builtin_bit_cast(bf16x8, x);
         }
     }
@@ -203,35 +202,70 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
 }
 
-// One workgroup per (sequence, query head); thread d owns output dim d.
+// One workgroup (256 threads) per (sequence, query head).  The chunk weights
+// w_c = 2^(lse2_c - M) are formed in parallel over chunks; then thread t sums
+// dim t % D over every (256 / D)-th chunk and the partial sums meet in LDS.
 template <int D>
-__global__ void __launch_bounds__(D)
+__global__ void __launch_bounds__(256)
 decode_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
                     const int32_t* __restrict__ lens, float* __restrict__ o,
                     float* __restrict__ lse, int Hq, int max_len, int nchunks) {
+    constexpr int NSPLIT = 256 / D;
+    __shared__ float wts[1024];
+    __shared__ float red[8];
+    __shared__ float part[NSPLIT][D];
     const int bh = blockIdx.x;
     const int b = bh / Hq;
-    const int d = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     int len = lens[b];
     len = len < 0 ? 0 : (len > max_len ? max_len : len);
     const int nc = (len + kCh - 1) / kCh;
     if (nc == 0) {  // no visible key: empty sum
-        o[(size_t)bh * D + d] = 0.f;
-        if (lse != nullptr && d == 0) lse[bh] = -INFINITY;
+        if (tid < D) o[(size_t)bh * D + tid] = 0.f;
+        if (lse != nullptr && tid == 0) lse[bh] = -INFINITY;
         return;
     }
     const float* lrow = ws_lse + (size_t)bh * nchunks;
     const float* orow = ws_o + (size_t)bh * nchunks * D;
+    // max over chunks
     float M = -INFINITY;
-    for (int c = 0; c < nc; ++c) M = fmaxf(M, lrow[c]);
-    float wsum = 0.f, acc = 0.f;
-    for (int c = 0; c < nc; ++c) {
+    for (int c = tid; c < nc; c += 256) M = fmaxf(M, lrow[c]);
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) M = fmaxf(M, __shfl_xor(M, sh));
+    if (lane == 0) red[wave] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    // weights and their sum (chunks beyond the LDS buffer are re-read below)
+    float ws = 0.f;
+    for (int c = tid; c < nc; c += 256) {
         const float w = fast_exp2(lrow[c] - M);
-        wsum += w;
+        if (c < 1024) wts[c] = w;
+        ws += w;
+    }
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) ws += __shfl_xor(ws, sh);
+    if (lane == 0) red[4 + wave] = ws;
+    __syncthreads();
+    const float wsum = red[4] + red[5] + red[6] + red[7];
+    const int d = tid % D;
+    const int j = tid / D;
+    float acc = 0.f;
+    for (int c = j; c < nc; c += NSPLIT) {
+        const float w = c < 1024 ? wts[c] : fast_exp2(lrow[c] - M);
         acc = fmaf(w, orow[(size_t)c * D + d], acc);
     }
-    o[(size_t)bh * D + d] = acc / wsum;
-    if (lse != nullptr && d == 0) lse[bh] = (M + fast_log2(wsum)) * kLn2;
+    part[j][d] = acc;
+    __syncthreads();
+    if (tid < D) {
+        float t = 0.f;
+#pragma unroll
+        for (int i = 0; i < NSPLIT; ++i) t += part[i][tid];
+        o[(size_t)bh * D + tid] = t / wsum;
+        if (lse != nullptr && tid == 0) lse[bh] = (M + fast_log2(wsum)) * kLn2;
+    }
 }
 
 template <int D, int GP>
@@ -257,7 +291,7 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     else if (G <= 8) e = launch_split<D, 8>(a, scale_log2, stream);
     else e = launch_split<D, 16>(a, scale_log2, stream);
     if (e != hipSuccess) return e;
-    decode_merge_kernel<D><<<(unsigned)(a.B * a.Hq), D, 0, stream>>>(
+    decode_merge_kernel<D><<<(unsigned)(a.B * a.Hq), 256, 0, stream>>>(
         a.ws_o, a.ws_lse, a.lens, a.o, a.lse, a.Hq, a.max_len, a.nchunks);
     return hipGetLastError();
 }

@@ -11,19 +11,30 @@
 // comparison table in "Transformer Architecture Breakdown", section 4.3 names.
 //
 // gfx950 mapping
-//   * workgroup = 4 waves; each wave owns 32 query rows of one query head.
-//     Waves of one workgroup cover the query heads of one KV head (GQA group),
-//     so each K/V tile is read from memory once per group of heads.
+//   * workgroup = 8 waves (two per SIMD); each wave owns 32 query rows of one
+//     query head.  The waves of a workgroup cover the query heads of one KV head
+//     (GQA group) and share every K/V tile, so a tile is read from memory once
+//     per group of heads.
+//   * K/V tiles of 64 keys are double-buffered in LDS: the next tile is loaded
+//     into registers while the current one is consumed, then stored, with one
+//     barrier per tile.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: in the 32x32 accumulator a lane
 //     holds one query (column) and 16 keys, so the row max and sum need one
 //     exchange between the two 32-lane halves.
 //   * O^T += V^T P^T on the same MFMA; P goes from the S accumulator into the B
 //     operand without leaving registers (the k-slot order is permuted the same
-//     way in both operands).  V is stored transposed in LDS for the A operand.
-//   * softmax in the exp2 domain: x = s * scale * log2(e) in fp32.
+//     way in both operands).  V stays row-major in LDS and the A operand is
+//     read with the gfx950 transposing LDS load (ds_read_b64_tr_b16).
+//   * softmax in the exp2 domain: p = 2^(s * scale * log2(e) - m) with one FMA
+//     and one v_exp_f32 per score.  The reference max m of a row moves only when
+//     the row max exceeds it by more than 8 (a factor 2^8), so most tiles skip
+//     the rescale of O and l; O and l always share one reference, so the result
+//     is the same exact recurrence.  O is divided by the sum of the bf16-rounded
+//     weights that entered the P V product (a true convex combination of V
+//     rows); the logsumexp uses the fp32 sum.
 //   * causal: tiles wholly above a wave's diagonal are skipped, the element mask
-//     is applied from the scores' key and query positions; heavy row blocks are
-//     launched first.
+//     is applied only on tiles that cross the diagonal or the end of K, and
+//     heavy row blocks are launched first.
 
 #include "device_common.h"
 #include "launch.h"
@@ -32,23 +43,43 @@ namespace attn {
 
 namespace {
 
-constexpr int kWaves = 4;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 8;   // 2 per SIMD
 constexpr int kRows = 32;   // query rows per wave
 constexpr int kBc = 64;     // keys per tile
-constexpr int kKPad = 8;    // bf16 elements of padding per K row in LDS
-constexpr int kVPad = 4;    // bf16 elements of padding per V^T row in LDS
+constexpr int kKPad = 8;    // K rows: stride = 4 banks mod 64, conflict-free 16-byte operand reads
+constexpr int kVPad = 32;   // V rows: stride = 16 banks mod 64, conflict-free transposed reads
+constexpr float kLazy = 8.f;  // keep the reference max until a row max exceeds it by 2^8
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// acc + lo + hi of a packed bf16 pair (v_dot2c_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float sum_bf16x2(uint32_t two, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, two), one, acc, false);
+}
+
+__device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(p));
+}
 
 template <int D, bool CAUSAL, bool ROPE>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(kWaves * 64, 1)
 prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, float* __restrict__ o,
                     float* __restrict__ lse, int B, int Hq, int Hkv, int Nq, int Nk,
                     float scale_log2, const double2* __restrict__ tab, int hpw, int wph,
                     int nchunks, int nrb) {
+    constexpr int NT = kWaves * 64;
     constexpr int KS = D + kKPad;       // K row stride in LDS (elements)
-    constexpr int VS = kBc + kVPad;     // V^T row stride in LDS (elements)
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[kBc * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VS];
+    constexpr int VS = D + kVPad;       // V row stride in LDS (elements)
+    constexpr int CPR = D / 8;          // 16-byte chunks per row
+    constexpr int LPT = kBc * CPR / NT; // chunks of K (and of V) per thread per tile
+    static_assert(LPT >= 1 && (kBc * CPR) % NT == 0, "tile/thread mismatch");
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBc * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBc * VS];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -82,7 +113,41 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     int kend = Nk;
     if (CAUSAL) kend = min(Nk, off + min(Nq, row0 + wph * kRows));
     const int ntiles = (kend + kBc - 1) / kBc;
+    const int wave_first = off + wrow0;                          // first row's position
     const int wave_last = off + min(Nq - 1, wrow0 + kRows - 1);  // last key this wave may see
+
+    const uint16_t* kbase = k + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+    const uint16_t* vbase = v + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+
+    // ---- tile loader: global -> registers -> LDS (row-major, padded)
+    uint4 pk[LPT], pv[LPT];
+    auto gload = [&](int key0) {
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+            const int c = tid + NT * i;
+            const int r = c / CPR;
+            const int col = (c - r * CPR) * 8;
+            uint4 xk = make_uint4(0, 0, 0, 0), xv = xk;
+            if (key0 + r < Nk) {
+                xk = *reinterpret_cast<const uint4*>(kbase + (size_t)(key0 + r) * D + col);
+                xv = *reinterpret_cast<const uint4*>(vbase + (size_t)(key0 + r) * D + col);
+            }
+            pk[i] = xk;
+            pv[i] = xv;
+        }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+            const int c = tid + NT * i;
+            const int r = c / CPR;
+            const int col = (c - r * CPR) * 8;
+            *reinterpret_cast<uint4*>(&Ks[buf][r * KS + col]) = pk[i];
+            *reinterpret_cast<uint4*>(&Vs[buf][r * VS + col]) = pv[i];
+        }
+    };
+
+    if (ntiles > 0) gload(0);
 
     // ---- Q fragment (B operand of S^T = K Q^T): query l32, d = 16s + 8*half .. +7
     bf16x8 qf[D / 16];
@@ -105,125 +170,123 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
-    float m_run = -INFINITY;
-    float l_run = 0.f;
+    float m_run = -INFINITY;   // reference max (log2 domain) of this lane's row
+    float l_run = 0.f;         // this lane's share of the row sum (fp32 weights): for lse
+    float r_run = 0.f;         // same sum of the bf16-rounded weights the MFMA used: for O
 
-    const uint16_t* kbase = k + ((size_t)b * Hkv + g) * (size_t)Nk * D;
-    const uint16_t* vbase = v + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+    // transposed-read addressing for the V operand (A of O^T += V^T P^T)
+    const int grp = lane >> 4;          // 16-lane group
+    const int w16 = lane & 15;
+    const int vrow_in = w16 >> 2;       // which of 4 keys this lane addresses
+    const int vcol_in = 16 * (grp & 1) + 4 * (w16 & 3);
+    const int vkey_h = 4 * (grp >> 1);  // = 4 * half
+
+    if (ntiles > 0) lstore(0);
+    __syncthreads();
 
     for (int t = 0; t < ntiles; ++t) {
         const int key0 = t * kBc;
-        __syncthreads();  // previous tile fully consumed
-        // ---- K tile -> LDS, row-major with padding
-#pragma unroll
-        for (int i = 0; i < (kBc * D / 8) / 256; ++i) {
-            const int c = tid + 256 * i;
-            const int r = c / (D / 8);
-            const int col = (c - r * (D / 8)) * 8;
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (key0 + r < Nk) x = *reinterpret_cast<const uint4*>(kbase + (size_t)(key0 + r) * D + col);
-            *reinterpret_cast<uint4*>(&Ks[r * KS + col]) = x;
-        }
-        // ---- V tile -> LDS transposed: thread takes 4 keys x 8 dims
-        if (tid < (kBc / 4) * (D / 8)) {
-            const int dc = tid % (D / 8);
-            const int kg = tid / (D / 8);
-            uint32_t w[4][4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = key0 + 4 * kg + r;
-                uint4 x = make_uint4(0, 0, 0, 0);
-                if (key < Nk) x = *reinterpret_cast<const uint4*>(vbase + (size_t)key * D + dc * 8);
-                w[r][0] = x.x; w[r][1] = x.y; w[r][2] = x.z; w[r][3] = x.w;
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int sh = (e & 1) ? 16 : 0;
-                const uint32_t a0 = (w[0][e >> 1] >> sh) & 0xffff;
-                const uint32_t a1 = (w[1][e >> 1] >> sh) & 0xffff;
-                const uint32_t a2 = (w[2][e >> 1] >> sh) & 0xffff;
-                const uint32_t a3 = (w[3][e >> 1] >> sh) & 0xffff;
-                uint2 pk = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
-                *reinterpret_cast<uint2*>(&Vt[(dc * 8 + e) * VS + 4 * kg]) = pk;
-            }
-        }
-        __syncthreads();
+        const int buf = t & 1;
+        const bool more = t + 1 < ntiles;
+        if (more) gload(key0 + kBc);  // next tile in flight during this tile's math
 
-        if (!active) continue;
-        if (CAUSAL && key0 > wave_last) continue;  // whole tile above this wave's diagonal
-
-        // ---- S^T = K Q^T : two 32-key blocks
-        f32x16 sacc[2];
+        if (active && !(CAUSAL && key0 > wave_last)) {
+            const uint16_t* Kt = Ks[buf];
+            const uint16_t* Vt = Vs[buf];
+            // ---- S^T = K Q^T : two 32-key blocks
+            f32x16 sacc[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            sacc[kb] = f32x16{};
+            for (int kb = 0; kb < 2; ++kb) {
+                sacc[kb] = f32x16{};
 #pragma unroll
-            for (int s = 0; s < D / 16; ++s) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + l32) * KS + 16 * s + 8 * half]);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
+                for (int s = 0; s < D / 16; ++s) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kt[(kb * 32 + l32) * KS + 16 * s + 8 * half]);
+                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
+                }
             }
-        }
-
-        // ---- scale, mask, online softmax (exp2 domain)
-        float mx = -INFINITY;
+            // ---- mask only tiles that cross the diagonal or the end of K
+            const bool need_mask = (key0 + kBc > Nk) || (CAUSAL && key0 + kBc - 1 > wave_first);
+            if (need_mask) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+                for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-                float x = sacc[kb][i] * scale_log2;
-                const bool vis = (key < Nk) && (!CAUSAL || key <= qpos);
-                x = vis ? x : -INFINITY;
-                sacc[kb][i] = x;
-                mx = fmaxf(mx, x);
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+                        const bool vis = (key < Nk) && (!CAUSAL || key <= qpos);
+                        sacc[kb][i] = vis ? sacc[kb][i] : -INFINITY;
+                    }
+                }
             }
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        float psum = 0.f;
+            // ---- row max of the raw scores (scale > 0 keeps the order)
+            float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = fast_exp2(sacc[kb][i] - m_use);
-                sacc[kb][i] = p;
-                psum += p;
+                for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[kb][i], sacc[kb][i + 1]));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_cand = mx * scale_log2;
+            // ---- lazy rescale: move the reference only when the max grew by > kLazy
+            const bool grow = m_cand > m_run + kLazy;
+            if (__ballot(grow)) {
+                const float m_new = grow ? m_cand : m_run;
+                const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
+                l_run *= alpha;
+                r_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+                m_run = m_new;
             }
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
+            const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+            float psum = 0.f;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float p = fast_exp2(fmaf(sacc[kb][i], scale_log2, neg_m));
+                    sacc[kb][i] = p;
+                    psum += p;
+                }
+            }
+            l_run += psum;
 
-        // ---- O^T += V^T P^T
+            // ---- O^T += V^T P^T
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-            for (int ss = 0; ss < 2; ++ss) {
-                uint4 pw;
-                pw.x = pack_bf16x2(sacc[kb][8 * ss + 0], sacc[kb][8 * ss + 1]);
-                pw.y = pack_bf16x2(sacc[kb][8 * ss + 2], sacc[kb][8 * ss + 3]);
-                pw.z = pack_bf16x2(sacc[kb][8 * ss + 4], sacc[kb][8 * ss + 5]);
-                pw.w = pack_bf16x2(sacc[kb][8 * ss + 6], sacc[kb][8 * ss + 7]);
-                const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-                const int kk = kb * 32 + 16 * ss + 4 * half;
+                for (int ss = 0; ss < 2; ++ss) {
+                    uint4 pw;
+                    pw.x = pack_bf16x2(sacc[kb][8 * ss + 0], sacc[kb][8 * ss + 1]);
+                    pw.y = pack_bf16x2(sacc[kb][8 * ss + 2], sacc[kb][8 * ss + 3]);
+                    pw.z = pack_bf16x2(sacc[kb][8 * ss + 4], sacc[kb][8 * ss + 5]);
+                    pw.w = pack_bf16x2(sacc[kb][8 * ss + 6], sacc[kb][8 * ss + 7]);
+                    const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+                    r_run = sum_bf16x2(pw.x, r_run);
+                    r_run = sum_bf16x2(pw.y, r_run);
+                    r_run = sum_bf16x2(pw.z, r_run);
+                    r_run = sum_bf16x2(pw.w, r_run);
+                    const int kbase_l = kb * 32 + 16 * ss + vkey_h + vrow_in;
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const uint16_t* vrow = &Vt[(32 * db + l32) * VS];
-                    const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kk);
-                    const uint2 hi = *reinterpret_cast<const uint2*>(vrow + kk + 8);
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
+                    for (int db = 0; db < D / 32; ++db) {
+                        const uint16_t* vp = Vt + kbase_l * VS + 32 * db + vcol_in;
+                        const s16x4 lo = lds_read_tr(vp);
+                        const s16x4 hi = lds_read_tr(vp + 8 * VS);
+                        const bf16x8 a = __builtin_bit_cast(
+                            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
+                    }
                 }
             }
         }
+        if (more) lstore(buf ^ 1);  // that buffer was last read before the previous barrier
+        __syncthreads();
     }
 
     if (!active || qi >= Nq) return;
+    // O is the convex combination with the weights the MFMA actually used (their
+    // bf16 roundings), so it is normalised by their sum; lse uses the fp32 sum.
     const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float inv = 1.f / l_tot;
+    const float r_tot = r_run + __shfl_xor(r_run, 32);
+    const float inv = 1.f / r_tot;
     float* orow = o + (((size_t)b * Hq + hq) * Nq + qi) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
@@ -251,7 +314,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     if (nwg == 0) return hipSuccess;
     if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
-    prefill_bf16_kernel<D, CAUSAL, ROPE><<<(unsigned)nwg, 256, 0, stream>>>(
+    prefill_bf16_kernel<D, CAUSAL, ROPE><<<(unsigned)nwg, kWaves * 64, 0, stream>>>(
         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
         static_cast<const uint16_t*>(a.v), a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, scale_log2,
         a.rope_tab, hpw, wph, nchunks, nrb);

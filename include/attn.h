@@ -60,7 +60,7 @@ typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_INVALID = 1,     /* bad argument: null pointer, negative size, Hq % Hkv,
                                  causal with Nq > Nk, non-finite scale, misaligned
-                                 pointer (16 bytes needed) ... */
+                                 pointer (16 bytes needed), scale <= 0 ... */
     ATTN_ERR_UNSUPPORTED = 2, /* valid but not built: d not in {64, 128}, f32 decode */
     ATTN_ERR_HIP = 3,         /* a HIP call or kernel launch failed */
     ATTN_ERR_WORKSPACE = 4    /* workspace missing or smaller than required */
@@ -83,7 +83,7 @@ size_t attn_fwd_workspace_bytes(int B, int Hkv, int Nk, int d, float rope_base,
  *   B, Hq, Hkv, Nq, Nk, d   sizes; B = 0, Hq = 0 or Nq = 0 is a no-op.
  *               Hkv >= 1, Hq % Hkv == 0, Nk >= 1, d in {64, 128}.
  *   causal      0 or 1.
- *   scale       finite multiplier of Q K^T (1/sqrt(d) for standard attention).
+ *   scale       finite multiplier of Q K^T, > 0 (1/sqrt(d) for standard attention).
  *   rope_base   0 = no RoPE, else a finite base > 0.
  *   workspace   device buffer of attn_fwd_workspace_bytes(...) bytes (may be
  *               NULL when that is 0); holds the rotated K during the call.
@@ -121,7 +121,8 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
 /*
  * RoPE on its own: out[b,h,n,:] = rotate(x[b,h,n,:], position pos_offset + n),
  * rounded to `dtype` exactly as attn_fwd rounds the rotated operands.
- * x, out  device [B, H, N, d] of `dtype` (may alias).  d even, d <= 256.
+ * x, out  device [B, H, N, d] of `dtype` (may alias).  d a multiple of 8
+ *         (bf16) or 4 (fp32), at most 512.
  */
 int attn_rope_apply(const void* x, void* out, int B, int H, int N, int d,
                     int pos_offset, float rope_base, attn_dtype dtype,

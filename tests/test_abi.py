@@ -60,7 +60,8 @@ def _fwd(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), 1), (dict(o=None), 1), (dict(B=-1), 1), (dict(Hkv=0), 1),
     (dict(Hq=6, Hkv=4), 1), (dict(causal=2), 1), (dict(Nq=9, Nk=8), 1),
-    (dict(Nk=0), 1), (dict(scale=float("inf")), 1), (dict(scale=float("nan")), 1),
+    (dict(Nk=0), 1), (dict(scale=float("inf")), 1), (dict(scale=float("nan")), 1), (dict(scale=0.0), 1),
+    (dict(scale=-0.5), 1),
     (dict(rope=-1.0), 1), (dict(rope=float("inf")), 1), (dict(dtype=7), 1),
     (dict(d=96), 2), (dict(d=32), 2), (dict(q=ctypes.c_void_p(258)), 1),
     (dict(rope=10000.0), 4), (dict(rope=10000.0, ws=P, wsb=100), 4),
@@ -85,7 +86,7 @@ def _dec(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(lens=None), 1), (dict(k=None), 1), (dict(Hq=6, Hkv=4), 1), (dict(max_len=0), 1),
-    (dict(scale=float("nan")), 1), (dict(dtype=esd.ATTN_F32), 2), (dict(d=80), 2),
+    (dict(scale=float("nan")), 1), (dict(scale=-1.0), 1), (dict(dtype=esd.ATTN_F32), 2), (dict(d=80), 2),
     (dict(ws=None), 4), (dict(wsb=10), 4), (dict(ws=ctypes.c_void_p(272)), 1),
 ])
 def test_decode_rejects_on_host(kw, code):
