@@ -132,26 +132,30 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
 
-    print("[bench] generating inputs", file=sys.stderr, flush=True)
-    q, k, v = W.fwd_inputs(w3)
-    dq, dk, dv = dev(q), dev(k), dev(v)
-    del q, k, v
-    o3 = torch.empty((w3.B, w3.Hq, w3.Nq, w3.d), dtype=torch.float32, device="cuda")
-    l3 = torch.empty((w3.B, w3.Hq, w3.Nq), dtype=torch.float32, device="cuda")
-    ws3 = torch.empty(esd.fwd_workspace_bytes(w3.B, w3.Hkv, w3.Nk, w3.d, w3.rope_base, esd.ATTN_BF16),
-                      dtype=torch.uint8, device="cuda")
-    lens = W.decode_lens(w4)
-    qd, kc, vc = W.decode_inputs(w4, lens)
-    dqd, dkc, dvc, dlens = dev(qd), dev(kc), dev(vc), dev(lens)
-    del qd, kc, vc
-    o4 = torch.empty((w4.B, w4.Hq, w4.d), dtype=torch.float32, device="cuda")
-    l4 = torch.empty((w4.B, w4.Hq), dtype=torch.float32, device="cuda")
-    ws4 = torch.empty(esd.decode_workspace_bytes(w4.B, w4.Hq, w4.Hkv, w4.max_len, w4.d),
-                      dtype=torch.uint8, device="cuda")
-    torch.cuda.synchronize()
-
     do_pf = args.only in (None, "prefill")
     do_dec = args.only in (None, "decode")
+
+    print("[bench] generating inputs", file=sys.stderr, flush=True)
+    flops = fwd_flops(w3)
+    lens = W.decode_lens(w4)
+    nbytes = decode_bytes(w4, lens)
+    if do_pf:
+        q, k, v = W.fwd_inputs(w3)
+        dq, dk, dv = dev(q), dev(k), dev(v)
+        del q, k, v
+        o3 = torch.empty((w3.B, w3.Hq, w3.Nq, w3.d), dtype=torch.float32, device="cuda")
+        l3 = torch.empty((w3.B, w3.Hq, w3.Nq), dtype=torch.float32, device="cuda")
+        ws3 = torch.empty(esd.fwd_workspace_bytes(w3.B, w3.Hkv, w3.Nk, w3.d, w3.rope_base,
+                                                  esd.ATTN_BF16), dtype=torch.uint8, device="cuda")
+    if do_dec:
+        qd, kc, vc = W.decode_inputs(w4, lens)
+        dqd, dkc, dvc, dlens = dev(qd), dev(kc), dev(vc), dev(lens)
+        del qd, kc, vc
+        o4 = torch.empty((w4.B, w4.Hq, w4.d), dtype=torch.float32, device="cuda")
+        l4 = torch.empty((w4.B, w4.Hq), dtype=torch.float32, device="cuda")
+        ws4 = torch.empty(esd.decode_workspace_bytes(w4.B, w4.Hq, w4.Hkv, w4.max_len, w4.d),
+                          dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
 
     def step(evs=None):
         if do_pf:
@@ -181,8 +185,6 @@ def main():
     pf_avg = float(np.mean(pf_ms))
     dec_avg = float(np.mean(dec_ms))
 
-    flops = fwd_flops(w3)
-    nbytes = decode_bytes(w4, lens)
     tflops = flops / (pf_avg * 1e-3) / 1e12 if do_pf else None
     gbs = nbytes / (dec_avg * 1e-3) / 1e9 if do_dec else None
 

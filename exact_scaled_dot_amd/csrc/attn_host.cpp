@@ -132,6 +132,8 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
     if (!known_dtype(dtype)) return fail(ATTN_ERR_INVALID, "unknown dtype");
     if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode is built for bf16");
     if (!supported_d(d)) return fail(ATTN_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+    if ((long long)max_len * d * 2 >= (1LL << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "one sequence's cache must be under 2 GiB (32-bit buffer offsets)");
     if (B == 0 || Hq == 0) return ATTN_OK;
     if (!q || !k_cache || !v_cache || !seq_lens || !o) return fail(ATTN_ERR_INVALID, "null pointer");
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))

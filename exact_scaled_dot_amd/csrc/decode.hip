@@ -13,14 +13,25 @@
 //   M = max_c lse2_c,  w_c = 2^(lse2_c - M),  O = sum_c w_c O_c / sum_c w_c,
 //   lse = (M + log2 sum_c w_c) * ln 2.
 //
-// gfx950 mapping of the split kernel (256 keys, one KV head, GP query heads):
-//   * S = K q^T on v_mfma_f32_16x16x32_bf16: A = 16 cached keys, B = the query
-//     heads of the group (columns), so every K row is read from memory once and
-//     serves all heads that share it.  For MFMA step s the four lanes that hold
-//     one key read its d range [32s, 32s + 32) (64 contiguous bytes); the same
-//     d-slot order is used for q, so the dot products are unchanged.
-//   * P V on the vector ALU: V rows stream in 16-byte pieces, weights come from
-//     LDS as broadcasts; partial sums are reduced across lanes, then waves.
+// gfx950 mapping of the split kernel (one KV head, up to 16 query heads,
+// 1024 keys: 128 per wave, 8 waves):
+//   * each wave streams its K rows and then its V rows in 32-key batches
+//     through a ring of four register slots (three batches always in flight,
+//     V loads start while the last K batches are in use); every load reads
+//     whole 256-byte rows and is unconditional, so the compiler keeps the
+//     batches in flight.
+//   * S = K q^T on v_mfma_f32_16x16x32_bf16 with the cached keys as rows and
+//     the group's query heads as columns, so each K row is read once for all
+//     heads that share it.  K rows go through a wave-private LDS slice; for
+//     MFMA step s the four lanes holding one key read its d range
+//     [32s, 32s + 32) there, and q uses the same d-slot order.  All scores of a wave stay in
+//     registers, so the per-head max is exact and nothing is rescaled.
+//   * V goes through a wave-private LDS slice and O = P V runs on the same MFMA: P (bf16) comes straight from the score
+//     registers as the A operand, the V operand is read with the transposing
+//     LDS load ds_read_b64_tr_b16.  O is normalised by the sum of the rounded
+//     weights (v_dot2c_f32_bf16), the log-sum by the fp32 sum.
+//   * the eight waves' partial states are merged in LDS with the same rule the
+//     merge kernel uses, giving one partial state per 1024-key chunk.
 
 #include "device_common.h"
 #include "launch.h"
@@ -29,23 +40,47 @@ namespace attn {
 
 namespace {
 
-constexpr int kCh = kDecodeChunk;  // keys per workgroup
-constexpr int kKeysPerWave = kCh / 4;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kCh = kDecodeChunk;       // keys per workgroup
+constexpr int kSplitWaves = 8;          // waves per split workgroup
+constexpr int kWaveKeys = kCh / kSplitWaves;  // keys per wave
+constexpr int kBatch = 32;              // keys per streamed batch
+constexpr int kNB = kWaveKeys / kBatch; // batches per wave
+
+__device__ __forceinline__ float sum_bf16x2(uint32_t two, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, two), one, acc, false);
+}
+
+__device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
+// Order this wave's LDS writes before its later LDS reads by other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 template <int D, int GP>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kSplitWaves * 64)
 decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, const int32_t* __restrict__ lens,
                     float* __restrict__ ws_o, float* __restrict__ ws_lse, int B, int Hq,
                     int Hkv, int max_len, float scale_log2, int nchunks, int nhch) {
     static_assert(D == 64 || D == 128, "head dim");
-    constexpr int NS = D / 32;          // MFMA k-steps over d
-    constexpr int NDC = D / 8;          // 16-byte pieces per row
-    constexpr int NKS = 64 / NDC;       // key slots per wave in the PV loop
-    __shared__ float Pl[kCh][GP];
-    __shared__ float redm[4][16];
-    __shared__ float reds[4][16];
-    __shared__ float accs[4][GP][D];
+    static_assert(GP >= 1 && GP <= 16, "heads per workgroup");
+    constexpr int NS = D / 32;          // QK MFMA k-steps over d
+    constexpr int NDB = D / 16;         // PV output blocks of 16 dims
+    constexpr int VSD = D + 16;         // V row stride in LDS: 8 banks mod 64
+    constexpr int KSD = D + 8;          // K row stride in LDS: 4 banks mod 64
+    constexpr int NW = kSplitWaves;
+    __shared__ __attribute__((aligned(16))) uint16_t Vl[NW][kBatch * VSD];
+    __shared__ float cm[NW][16], cl[NW][16], cr[NW][16];
+    __shared__ float co[NW][GP][D];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -53,9 +88,12 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const int r16 = lane & 15;
     const int quarter = lane >> 4;
 
-    int idx = blockIdx.x;
-    const int c = idx % nchunks;
-    idx /= nchunks;
+    // Chunk-major order: all first chunks of every (sequence, KV head) come first,
+    // so the workgroups past a sequence's end (which exit at once) are not
+    // interleaved with the heavy ones.
+    const int per_c = B * Hkv * nhch;
+    const int c = blockIdx.x / per_c;
+    int idx = blockIdx.x - c * per_c;
     const int hch = idx % nhch;
     idx /= nhch;
     const int g = idx % Hkv;
@@ -72,133 +110,185 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const size_t kvoff = ((size_t)b * Hkv + g) * (size_t)max_len * D;
     const uint16_t* kb = k + kvoff;
     const uint16_t* vb = v + kvoff;
-    const int wk0 = k0 + wave * kKeysPerWave;    // first key of this wave
+    const int wk0 = k0 + wave * kWaveKeys;             // first key of this wave
+    const int wn = max(0, min(kWaveKeys, len - wk0));  // keys of this wave
 
-    // ---- issue all K and V loads of this wave's keys
-    uint4 kf[4][NS];
+    // ---- one stream per wave: K batches 0..kNB-1, then V batches 0..kNB-1, each
+    //      32 keys x D bf16 = VPL 16-byte pieces per lane, through a ring of
+    //      NSLOT register slots, so NSLOT-1 batches are in flight (V loads start
+    //      while the last K batches are still being used).
+    constexpr int VPL = kBatch * (D / 8) / 64;
+    static_assert(VPL == 2 * NS, "a K batch and a V batch fill the same slot");
+    constexpr int NSLOT = 4;
+    u32x4 ring[NSLOT][VPL];
+    // Piece j of batch bi (K or V): key 32*bi + (lane + 64j) / (D/8),
+    // d 8*((lane + 64j) % (D/8)): every load instruction reads whole rows.
+    // Buffer loads: the base sits in a scalar resource whose size is the
+    // sequence's valid rows, a lane only holds a 32-bit offset, and rows past
+    // the end come back as zeros (finite data; their scores are masked to
+    // -inf, so their weights are exactly 0).  The loads are unconditional, so
+    // the compiler can count them in flight.
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kb), (short)0, len * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(vb), (short)0, len * D * 2, 0x00020000);
+    const int lane_off = (lane / (D / 8)) * D * 2 + (lane % (D / 8)) * 16;  // bytes
+    constexpr int JSTEP = 64 / (D / 8) * D * 2;                               // bytes per j
+    auto sload = [&](int e, int slot) {
+        const int boff = (wk0 + kBatch * (e < kNB ? e : e - kNB)) * D * 2 + lane_off;
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-        const int key = wk0 + 16 * grp + r16;
+        for (int j = 0; j < VPL; ++j)
+            ring[slot][j] = __builtin_amdgcn_raw_buffer_load_b128(e < kNB ? rk : rv, boff + JSTEP * j, 0, 0);
+    };
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (key < len) x = *reinterpret_cast<const uint4*>(kb + (size_t)key * D + 32 * s + 8 * quarter);
-            kf[grp][s] = x;
-        }
-    }
-    const int dc = lane % NDC;
-    const int ks = lane / NDC;
-    uint4 vf[kKeysPerWave / NKS];
-#pragma unroll
-    for (int it = 0; it < kKeysPerWave / NKS; ++it) {
-        const int key = wk0 + ks + NKS * it;
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (key < len) x = *reinterpret_cast<const uint4*>(vb + (size_t)key * D + 8 * dc);
-        vf[it] = x;
-    }
+    for (int e = 0; e < NSLOT - 1; ++e) sload(e, e);
 
-    // ---- q operand: column r16 = head, k-slots 8*quarter.. = d 32s + 8*quarter ..
+    // ---- q operand (B of S = K q^T): column r16 = head, d-slots 32s + 8*quarter ..
+    //      (columns past the last head read a valid head and are zeroed)
     bf16x8 qf[NS];
     {
         const bool ok = r16 < nh;
-        const uint16_t* qrow = q + ((size_t)b * Hq + h0 + (ok ? r16 : 0)) * D;
+        const uint16_t* qrow = q + ((size_t)b * Hq + h0 + min(r16, nh - 1)) * D;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (ok) x = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * quarter);
+            uint4 x = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * quarter);
+            if (!ok) x = make_uint4(0, 0, 0, 0);
             qf[s] = __builtin_bit_cast(bf16x8, x);
         }
     }
 
-    // ---- scores: lane holds head r16, keys 16*grp + 4*quarter + i
-    float sc[4][4];
-    float mx = -INFINITY;
+    // ---- pass over K: scores.  Lane holds head r16, keys 32*bi + 16*grp + 4*quarter + i.
+    //      K rows go through the wave's LDS slice (row stride D + 8: 4 banks apart,
+    //      so the 16-byte operand reads of 16 rows hit distinct banks).
+    uint16_t* vl = Vl[wave];
+    float sc[kNB][8];
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-        f32x4 acc = f32x4{};
+    for (int bi = 0; bi < kNB; ++bi) {
+        __builtin_amdgcn_sched_barrier(0);  // keep each batch's loads where the ring puts them
+        sload(bi + NSLOT - 1, (bi + NSLOT - 1) % NSLOT);
+        wave_lds_sync();  // the previous batch's operand reads are done
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[grp][s]), qf[s], acc, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = wk0 + 16 * grp + 4 * quarter + i;
-            const float x = key < len ? acc[i] * scale_log2 : -INFINITY;
-            sc[grp][i] = x;
-            mx = fmaxf(mx, x);
+        for (int j = 0; j < VPL; ++j) {
+            const int cc = lane + 64 * j;
+            const int kr = cc / (D / 8);
+            *reinterpret_cast<u32x4*>(vl + kr * KSD + (cc - kr * (D / 8)) * 8) = ring[bi % NSLOT][j];
         }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (lane < 16) redm[wave][lane] = mx;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(redm[0][r16], redm[1][r16]), fmaxf(redm[2][r16], redm[3][r16]));
-    // M is finite: key k0 < len is visible in every workgroup that runs
-    float ls = 0.f;
+        wave_lds_sync();
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
+        for (int grp = 0; grp < 2; ++grp) {
+            f32x4 acc = f32x4{};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float p = fast_exp2(sc[grp][i] - M);
-            ls += p;
-            if (r16 < GP) Pl[wave * kKeysPerWave + 16 * grp + 4 * quarter + i][r16] = p;
-        }
-    }
-    ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
-    if (lane < 16) reds[wave][lane] = ls;
-    __syncthreads();  // Pl and reds complete
-
-    // ---- P V on the vector ALU: lane takes 8 dims (dc) of keys ks, ks+NKS, ...
-    float acc[GP][8];
+            for (int s = 0; s < NS; ++s) {
+                const u32x4 kx = *reinterpret_cast<const u32x4*>(vl + (16 * grp + r16) * KSD + 32 * s + 8 * quarter);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kx), qf[s], acc, 0, 0, 0);
+            }
 #pragma unroll
-    for (int h = 0; h < GP; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-#pragma unroll
-    for (int it = 0; it < kKeysPerWave / NKS; ++it) {
-        const int kl = wave * kKeysPerWave + ks + NKS * it;
-        float pw[GP];
-#pragma unroll
-        for (int h = 0; h < GP; ++h) pw[h] = Pl[kl][h];
-        const uint32_t w[4] = {vf[it].x, vf[it].y, vf[it].z, vf[it].w};
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-            const float x0 = bf16_lo(w[e2]);
-            const float x1 = bf16_hi(w[e2]);
-#pragma unroll
-            for (int h = 0; h < GP; ++h) {
-                acc[h][2 * e2] = fmaf(pw[h], x0, acc[h][2 * e2]);
-                acc[h][2 * e2 + 1] = fmaf(pw[h], x1, acc[h][2 * e2 + 1]);
+            for (int i = 0; i < 4; ++i) {
+                const int key = kBatch * bi + 16 * grp + 4 * quarter + i;
+                sc[bi][4 * grp + i] = key < wn ? acc[i] : -INFINITY;
             }
         }
     }
-    // reduce over the key slots of a wave (lanes sharing dc)
+
+    // ---- exact per-head max of this wave, weights, sums
+    float mx = -INFINITY;
 #pragma unroll
-    for (int sh = NDC; sh < 64; sh <<= 1) {
+    for (int bi = 0; bi < kNB; ++bi)
 #pragma unroll
-        for (int h = 0; h < GP; ++h)
+        for (int j = 0; j < 8; j += 2) mx = fmaxf(mx, fmaxf(sc[bi][j], sc[bi][j + 1]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m2 = mx * scale_log2;                  // -inf when the wave has no key
+    const float neg = (m2 == -INFINITY) ? 0.f : -m2;
+    float lsum = 0.f, rsum = 0.f;
+    uint4 pa[kNB];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], sh);
+    for (int bi = 0; bi < kNB; ++bi) {
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            p[j] = fast_exp2(fmaf(sc[bi][j], scale_log2, neg));
+            lsum += p[j];
+        }
+        pa[bi].x = pack_bf16x2(p[0], p[1]);
+        pa[bi].y = pack_bf16x2(p[2], p[3]);
+        pa[bi].z = pack_bf16x2(p[4], p[5]);
+        pa[bi].w = pack_bf16x2(p[6], p[7]);
+        rsum = sum_bf16x2(pa[bi].x, rsum);
+        rsum = sum_bf16x2(pa[bi].y, rsum);
+        rsum = sum_bf16x2(pa[bi].z, rsum);
+        rsum = sum_bf16x2(pa[bi].w, rsum);
     }
-    if (ks == 0) {
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    rsum += __shfl_xor(rsum, 16);
+    rsum += __shfl_xor(rsum, 32);
+
+    // ---- pass over V: O = P V.  Lane output: head 4*quarter + i, dim 16*db + r16.
+    f32x4 oacc[NDB];
 #pragma unroll
-        for (int h = 0; h < GP; ++h)
+    for (int db = 0; db < NDB; ++db) oacc[db] = f32x4{};
+    const int w16 = lane & 15;
+    const int trow = 4 * quarter + (w16 >> 2);  // key row this lane addresses
+    const int tcol = 4 * (w16 & 3);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) accs[wave][h][8 * dc + e] = acc[h][e];
+    for (int bi = 0; bi < kNB; ++bi) {
+        const int e = kNB + bi;
+        __builtin_amdgcn_sched_barrier(0);
+        if (e + NSLOT - 1 < 2 * kNB) sload(e + NSLOT - 1, (e + NSLOT - 1) % NSLOT);
+        wave_lds_sync();  // previous batch's reads are done before it is overwritten
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            const int cc = lane + 64 * j;
+            const int kr = cc / (D / 8);
+            const int col = (cc - kr * (D / 8)) * 8;
+            *reinterpret_cast<u32x4*>(vl + kr * VSD + col) = ring[e % NSLOT][j];
+        }
+        wave_lds_sync();
+        const bf16x8 a = __builtin_bit_cast(bf16x8, pa[bi]);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const uint16_t* vp = vl + trow * VSD + 16 * db + tcol;
+            const s16x4 lo = lds_read_tr(vp);
+            const s16x4 hi = lds_read_tr(vp + 16 * VSD);
+            const bf16x8 bv = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, oacc[db], 0, 0, 0);
+        }
+    }
+
+    // ---- merge the four waves' states in LDS
+    if (quarter == 0) {
+        cm[wave][r16] = m2;
+        cl[wave][r16] = lsum;
+        cr[wave][r16] = rsum;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int h = 4 * quarter + i;
+        if (h < GP) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) co[wave][h][16 * db + r16] = oacc[db][i];
+        }
     }
     __syncthreads();
-    // ---- combine the 4 waves and write the chunk's partial state
-    for (int i = tid; i < nh * D; i += 256) {
+    for (int i = tid; i < nh * D; i += NW * 64) {
         const int h = i / D;
         const int d = i - h * D;
-        const float lsum = reds[0][h] + reds[1][h] + reds[2][h] + reds[3][h];
-        const float ov = (accs[0][h][d] + accs[1][h][d] + accs[2][h][d] + accs[3][h][d]) / lsum;
-        const size_t row = ((size_t)b * Hq + h0 + h) * nchunks + c;
-        ws_o[row * D + d] = ov;
-        if (d == 0) {
-            const float Mh = fmaxf(fmaxf(redm[0][h], redm[1][h]), fmaxf(redm[2][h], redm[3][h]));
-            ws_lse[row] = Mh + fast_log2(lsum);
+        float M = cm[0][h];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) M = fmaxf(M, cm[w][h]);
+        float acc = 0.f, rs = 0.f, ls = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float f = fast_exp2(cm[w][h] - M);  // 0 for a wave without keys
+            acc = fmaf(f, co[w][h][d], acc);
+            rs = fmaf(f, cr[w][h], rs);
+            ls = fmaf(f, cl[w][h], ls);
         }
+        const size_t row = ((size_t)b * Hq + h0 + h) * nchunks + c;
+        ws_o[row * D + d] = acc / rs;
+        if (d == 0) ws_lse[row] = M + fast_log2(ls);
     }
 }
 
@@ -253,7 +343,18 @@ decode_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
     const int d = tid % D;
     const int j = tid / D;
     float acc = 0.f;
-    for (int c = j; c < nc; c += NSPLIT) {
+    int c = j;
+    for (; c + 7 * NSPLIT < nc; c += 8 * NSPLIT) {  // eight loads in flight
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = orow[(size_t)(c + u * NSPLIT) * D + d];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int cu = c + u * NSPLIT;
+            acc = fmaf(cu < 1024 ? wts[cu] : fast_exp2(lrow[cu] - M), x[u], acc);
+        }
+    }
+    for (; c < nc; c += NSPLIT) {
         const float w = c < 1024 ? wts[c] : fast_exp2(lrow[c] - M);
         acc = fmaf(w, orow[(size_t)c * D + d], acc);
     }
@@ -274,7 +375,7 @@ hipError_t launch_split(const DecodeArgs& a, float scale_log2, hipStream_t strea
     const int nhch = (G + GP - 1) / GP;
     const long long nwg = (long long)a.nchunks * nhch * a.Hkv * a.B;
     if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    decode_split_kernel<D, GP><<<(unsigned)nwg, 256, 0, stream>>>(
+    decode_split_kernel<D, GP><<<(unsigned)nwg, kSplitWaves * 64, 0, stream>>>(
         a.q, a.k, a.v, a.lens, a.ws_o, a.ws_lse, a.B, a.Hq, a.Hkv, a.max_len, scale_log2,
         a.nchunks, nhch);
     return hipGetLastError();

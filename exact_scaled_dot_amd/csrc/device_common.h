@@ -9,6 +9,7 @@ namespace attn {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in registers
 
 constexpr float kLn2 = 0.693147180559945309f;
 

@@ -43,7 +43,7 @@ struct DecodeArgs {
     int nchunks;
 };
 
-constexpr int kDecodeChunk = 256;  // keys per split workgroup
+constexpr int kDecodeChunk = 1024;  // keys per split workgroup
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 

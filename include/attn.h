@@ -61,7 +61,8 @@ typedef enum {
     ATTN_ERR_INVALID = 1,     /* bad argument: null pointer, negative size, Hq % Hkv,
                                  causal with Nq > Nk, non-finite scale, misaligned
                                  pointer (16 bytes needed), scale <= 0 ... */
-    ATTN_ERR_UNSUPPORTED = 2, /* valid but not built: d not in {64, 128}, f32 decode */
+    ATTN_ERR_UNSUPPORTED = 2, /* valid but not built: d not in {64, 128}, f32 decode,
+                                 a decode cache row range of 2 GiB or more */
     ATTN_ERR_HIP = 3,         /* a HIP call or kernel launch failed */
     ATTN_ERR_WORKSPACE = 4    /* workspace missing or smaller than required */
 } attn_status;
@@ -110,7 +111,8 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int d);
  *              of 0 yields O = 0 and lse = -inf.
  *   o          device fp32 [B, Hq, d];  lse  device fp32 [B, Hq] or NULL.
  *   workspace  device buffer of attn_decode_workspace_bytes(...) bytes.
- * dtype must be ATTN_BF16 (ATTN_F32 returns ATTN_ERR_UNSUPPORTED).
+ * dtype must be ATTN_BF16 (ATTN_F32 returns ATTN_ERR_UNSUPPORTED); one
+ * sequence's K (or V) rows, max_len * d * 2 bytes, must stay under 2 GiB.
  */
 int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* seq_lens, float* o, float* lse,

@@ -40,7 +40,7 @@ def test_workspace_sizes():
     assert esd.fwd_workspace_bytes(2, 8, 8192, 128, 10000.0, esd.ATTN_BF16) == 2 * 8 * 8192 * 128 * 2
     assert esd.fwd_workspace_bytes(1, 1, 256, 64, 100.0, esd.ATTN_F32) == 256 * 64 * 4
     n = esd.decode_workspace_bytes(32, 32, 8, 32768, 128)
-    rows = 32 * 32 * (32768 // 256)
+    rows = 32 * 32 * (32768 // 1024)  # one partial state per 1024-key chunk
     assert n >= rows * 129 * 4 and n < rows * 129 * 4 + 256
     assert esd.decode_workspace_bytes(0, 32, 8, 32768, 128) == 0
 
@@ -88,6 +88,7 @@ def _dec(**kw):
     (dict(lens=None), 1), (dict(k=None), 1), (dict(Hq=6, Hkv=4), 1), (dict(max_len=0), 1),
     (dict(scale=float("nan")), 1), (dict(scale=-1.0), 1), (dict(dtype=esd.ATTN_F32), 2), (dict(d=80), 2),
     (dict(ws=None), 4), (dict(wsb=10), 4), (dict(ws=ctypes.c_void_p(272)), 1),
+    (dict(max_len=1 << 23), 2),
 ])
 def test_decode_rejects_on_host(kw, code):
     assert _dec(**kw) == code

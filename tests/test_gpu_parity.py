@@ -185,11 +185,12 @@ def test_c4_full():
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (32, 8), (16, 2), (32, 1), (12, 4), (64, 2)])
 @pytest.mark.parametrize("d", [64, 128])
 def test_decode_shapes(Hq, Hkv, d):
-    """Lengths 0, 1, chunk edges and a NaN-poisoned tail past each length."""
+    """Lengths 0, 1, batch / wave / chunk edges (32, 128, 1024 keys), several
+    chunks, and a NaN-poisoned tail past each length."""
     import torch
     w = W.WORKLOADS["c4"]
-    lens = np.array([0, 1, 255, 256, 257, 511, 700, 1000], dtype=np.int32)
-    q, kc, vc = W.decode_inputs(w, lens, Hq=Hq, Hkv=Hkv, max_len=1024, d=d, seed_base=7600 + Hq)
+    lens = np.array([0, 1, 31, 33, 127, 129, 1023, 1024, 1025, 2100, 3000], dtype=np.int32)
+    q, kc, vc = W.decode_inputs(w, lens, Hq=Hq, Hkv=Hkv, max_len=3000, d=d, seed_base=7600 + Hq)
     o, lse = esd.decode(dev(q), dev(kc), dev(vc), dev(lens), scale=1 / math.sqrt(d))
     torch.cuda.synchronize()
     o, lse = host(o), host(lse)
