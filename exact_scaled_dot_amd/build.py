@@ -22,6 +22,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["attn_host.cpp", "rope.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip"]
 
+# Per-source extra flags.  The bf16 kernels never see NaN (inputs are finite by
+# contract; masking uses -inf), so max chains need no NaN canonicalisation and
+# fold into v_max3_f32.
+EXTRA = {"prefill_bf16.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"]}
+
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -31,7 +36,7 @@ COMMON = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -17,12 +17,20 @@ constexpr float kLn2 = 0.693147180559945309f;
 __device__ __forceinline__ float bf16_lo(uint32_t two) { return __uint_as_float(two << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t two) { return __uint_as_float(two & 0xffff0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 bits (a in the low half), round to nearest even:
+// one gfx950 v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    __bf16 x = (__bf16)a;
-    __bf16 y = (__bf16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+
+// An empty volatile asm statement: code in a branch that holds it cannot be
+// speculated, so cheap-looking vector work (64 multiplies, 32 selects) stays
+// behind its wave-uniform branch.
+__device__ __forceinline__ void keep_branch() { __asm__ volatile(""); }
 
 // One RoPE pair in fp64, products and sums rounded separately (no contraction),
 // then fp64 -> fp32 (nearest even).  Caller rounds on to bf16 if needed.

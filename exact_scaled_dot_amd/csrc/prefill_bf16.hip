@@ -207,6 +207,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             // ---- mask only tiles that cross the diagonal or the end of K
             const bool need_mask = (key0 + kBc > Nk) || (CAUSAL && key0 + kBc - 1 > wave_first);
             if (need_mask) {
+                keep_branch();
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -228,6 +229,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             // ---- lazy rescale: move the reference only when the max grew by > kLazy
             const bool grow = m_cand > m_run + kLazy;
             if (__ballot(grow)) {
+                keep_branch();
                 const float m_new = grow ? m_cand : m_run;
                 const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
                 l_run *= alpha;
