@@ -72,6 +72,8 @@ int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
         return fail(ATTN_ERR_INVALID, "rope_base must be 0 or a finite positive base");
     if (!known_dtype(dtype)) return fail(ATTN_ERR_INVALID, "unknown dtype");
     if (!supported_d(d)) return fail(ATTN_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+    if ((long long)Nk * d * 4 >= (1LL << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "one head's K (or V) must be under 2 GiB (32-bit buffer offsets)");
     if (B == 0 || Hq == 0 || Nq == 0) return ATTN_OK;
     if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID, "null pointer");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))

@@ -15,9 +15,11 @@
 //     query head.  The waves of a workgroup cover the query heads of one KV head
 //     (GQA group) and share every K/V tile, so a tile is read from memory once
 //     per group of heads.
-//   * K/V tiles of 64 keys are double-buffered in LDS: the next tile is loaded
-//     into registers while the current one is consumed, then stored, with one
-//     barrier per tile.
+//   * K/V tiles of 64 keys are double-buffered in LDS, with K one tile ahead
+//     of V: iteration t forms the scores of tile t+1 on the matrix cores while
+//     the vector ALU runs the softmax of tile t, then accumulates P V of tile t.
+//     The tiles two (K) and one (V) ahead are loaded into registers during the
+//     iteration and stored afterwards, with one barrier per tile.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: in the 32x32 accumulator a lane
 //     holds one query (column) and 16 keys, so the row max and sum need one
 //     exchange between the two 32-lane halves.
@@ -32,9 +34,9 @@
 //     is the same exact recurrence.  O is divided by the sum of the bf16-rounded
 //     weights that entered the P V product (a true convex combination of V
 //     rows); the logsumexp uses the fp32 sum.
-//   * causal: tiles wholly above a wave's diagonal are skipped, the element mask
-//     is applied only on tiles that cross the diagonal or the end of K, and
-//     heavy row blocks are launched first.
+//   * causal: a workgroup stops at the last tile its rows can see, the element
+//     mask is applied only on tiles that cross a wave's diagonal or the end of
+//     K, and heavy row blocks are launched first.
 
 #include "device_common.h"
 #include "launch.h"
@@ -119,35 +121,37 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const uint16_t* kbase = k + ((size_t)b * Hkv + g) * (size_t)Nk * D;
     const uint16_t* vbase = v + ((size_t)b * Hkv + g) * (size_t)Nk * D;
 
-    // ---- tile loader: global -> registers -> LDS (row-major, padded)
-    uint4 pk[LPT], pv[LPT];
-    auto gload = [&](int key0) {
+    // ---- tile loaders: global -> registers -> LDS (row-major, padded).
+    //      K runs one tile ahead of V: while tile t's softmax runs, the scores of
+    //      tile t+1 are already being formed on the matrix cores.  Buffer loads:
+    //      the scalar resource spans this head's Nk rows, so rows past the end
+    //      read as zeros and no load needs a branch.
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kbase), (short)0, Nk * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(vbase), (short)0, Nk * D * 2, 0x00020000);
+    u32x4 pk[LPT], pv[LPT];
+    auto gload = [&](u32x4 (&dst)[LPT], __amdgpu_buffer_rsrc_t rsrc, int key0) {
 #pragma unroll
         for (int i = 0; i < LPT; ++i) {
             const int c = tid + NT * i;
             const int r = c / CPR;
             const int col = (c - r * CPR) * 8;
-            uint4 xk = make_uint4(0, 0, 0, 0), xv = xk;
-            if (key0 + r < Nk) {
-                xk = *reinterpret_cast<const uint4*>(kbase + (size_t)(key0 + r) * D + col);
-                xv = *reinterpret_cast<const uint4*>(vbase + (size_t)(key0 + r) * D + col);
-            }
-            pk[i] = xk;
-            pv[i] = xv;
+            dst[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, ((key0 + r) * D + col) * 2, 0, 0);
         }
     };
-    auto lstore = [&](int buf) {
+    auto lstore = [&](const u32x4 (&src)[LPT], uint16_t* dstbuf, int stride) {
 #pragma unroll
         for (int i = 0; i < LPT; ++i) {
             const int c = tid + NT * i;
             const int r = c / CPR;
             const int col = (c - r * CPR) * 8;
-            *reinterpret_cast<uint4*>(&Ks[buf][r * KS + col]) = pk[i];
-            *reinterpret_cast<uint4*>(&Vs[buf][r * VS + col]) = pv[i];
+            *reinterpret_cast<u32x4*>(&dstbuf[r * stride + col]) = src[i];
         }
     };
 
-    if (ntiles > 0) gload(0);
+    gload(pk, rk, 0);
+    gload(pv, rv, 0);
 
     // ---- Q fragment (B operand of S^T = K Q^T): query l32, d = 16s + 8*half .. +7
     bf16x8 qf[D / 16];
@@ -181,106 +185,117 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const int vcol_in = 16 * (grp & 1) + 4 * (w16 & 3);
     const int vkey_h = 4 * (grp >> 1);  // = 4 * half
 
-    if (ntiles > 0) lstore(0);
+    // S^T = K Q^T for one 64-key tile held in LDS
+    auto qk = [&](const uint16_t* Kt, f32x16 (&sacc)[2]) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            sacc[kb] = f32x16{};
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kt[(kb * 32 + l32) * KS + 16 * s + 8 * half]);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
+            }
+        }
+    };
+
+    // prologue: K(0), V(0) and K(1) in LDS, S(0) formed
+    f32x16 scur[2], snext[2];
+    lstore(pk, Ks[0], KS);
+    lstore(pv, Vs[0], VS);
+    gload(pk, rk, kBc);
+    lstore(pk, Ks[1], KS);
     __syncthreads();
+    qk(Ks[0], scur);
 
     for (int t = 0; t < ntiles; ++t) {
         const int key0 = t * kBc;
-        const int buf = t & 1;
-        const bool more = t + 1 < ntiles;
-        if (more) gload(key0 + kBc);  // next tile in flight during this tile's math
-
-        if (active && !(CAUSAL && key0 > wave_last)) {
-            const uint16_t* Kt = Ks[buf];
-            const uint16_t* Vt = Vs[buf];
-            // ---- S^T = K Q^T : two 32-key blocks
-            f32x16 sacc[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                sacc[kb] = f32x16{};
-#pragma unroll
-                for (int s = 0; s < D / 16; ++s) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kt[(kb * 32 + l32) * KS + 16 * s + 8 * half]);
-                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
-                }
-            }
-            // ---- mask only tiles that cross the diagonal or the end of K
-            const bool need_mask = (key0 + kBc > Nk) || (CAUSAL && key0 + kBc - 1 > wave_first);
-            if (need_mask) {
-                keep_branch();
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-                        const bool vis = (key < Nk) && (!CAUSAL || key <= qpos);
-                        sacc[kb][i] = vis ? sacc[kb][i] : -INFINITY;
-                    }
-                }
-            }
-            // ---- row max of the raw scores (scale > 0 keeps the order)
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[kb][i], sacc[kb][i + 1]));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_cand = mx * scale_log2;
-            // ---- lazy rescale: move the reference only when the max grew by > kLazy
-            const bool grow = m_cand > m_run + kLazy;
-            if (__ballot(grow)) {
-                keep_branch();
-                const float m_new = grow ? m_cand : m_run;
-                const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
-                l_run *= alpha;
-                r_run *= alpha;
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-                m_run = m_new;
-            }
-            const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
-            float psum = 0.f;
+        // ---- short prologue (may branch): mask, row max, rare rescale
+        const bool need_mask = (key0 + kBc > Nk) || (CAUSAL && key0 + kBc - 1 > wave_first);
+        if (need_mask) {
+            keep_branch();
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float p = fast_exp2(fmaf(sacc[kb][i], scale_log2, neg_m));
-                    sacc[kb][i] = p;
-                    psum += p;
-                }
-            }
-            l_run += psum;
-
-            // ---- O^T += V^T P^T
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int ss = 0; ss < 2; ++ss) {
-                    uint4 pw;
-                    pw.x = pack_bf16x2(sacc[kb][8 * ss + 0], sacc[kb][8 * ss + 1]);
-                    pw.y = pack_bf16x2(sacc[kb][8 * ss + 2], sacc[kb][8 * ss + 3]);
-                    pw.z = pack_bf16x2(sacc[kb][8 * ss + 4], sacc[kb][8 * ss + 5]);
-                    pw.w = pack_bf16x2(sacc[kb][8 * ss + 6], sacc[kb][8 * ss + 7]);
-                    const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-                    r_run = sum_bf16x2(pw.x, r_run);
-                    r_run = sum_bf16x2(pw.y, r_run);
-                    r_run = sum_bf16x2(pw.z, r_run);
-                    r_run = sum_bf16x2(pw.w, r_run);
-                    const int kbase_l = kb * 32 + 16 * ss + vkey_h + vrow_in;
-#pragma unroll
-                    for (int db = 0; db < D / 32; ++db) {
-                        const uint16_t* vp = Vt + kbase_l * VS + 32 * db + vcol_in;
-                        const s16x4 lo = lds_read_tr(vp);
-                        const s16x4 hi = lds_read_tr(vp + 8 * VS);
-                        const bf16x8 a = __builtin_bit_cast(
-                            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
-                    }
+                    const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+                    const bool vis = (key < Nk) && (!CAUSAL || key <= qpos);
+                    scur[kb][i] = vis ? scur[kb][i] : -INFINITY;
                 }
             }
         }
-        if (more) lstore(buf ^ 1);  // that buffer was last read before the previous barrier
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(scur[kb][i], scur[kb][i + 1]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_cand = mx * scale_log2;
+        const bool grow = m_cand > m_run + kLazy;
+        if (__ballot(grow)) {
+            keep_branch();
+            const float m_new = grow ? m_cand : m_run;
+            const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
+            l_run *= alpha;
+            r_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+            m_run = m_new;
+        }
+        const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+
+        // ---- main block, no branches: next tile's scores on the matrix cores,
+        //      this tile's weights on the vector ALU, then P V.
+        gload(pk, rk, key0 + 2 * kBc);  // K(t+2) in flight (zeros past the end)
+        gload(pv, rv, key0 + kBc);      // V(t+1) in flight
+        qk(Ks[(t + 1) & 1], snext);
+        const uint16_t* Vt = Vs[t & 1];
+        float psum = 0.f;
+        uint4 pw[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int ss = 0; ss < 2; ++ss) {
+                float p[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    p[e] = fast_exp2(fmaf(scur[kb][8 * ss + e], scale_log2, neg_m));
+                    psum += p[e];
+                }
+                pw[kb][ss].x = pack_bf16x2(p[0], p[1]);
+                pw[kb][ss].y = pack_bf16x2(p[2], p[3]);
+                pw[kb][ss].z = pack_bf16x2(p[4], p[5]);
+                pw[kb][ss].w = pack_bf16x2(p[6], p[7]);
+                r_run = sum_bf16x2(pw[kb][ss].x, r_run);
+                r_run = sum_bf16x2(pw[kb][ss].y, r_run);
+                r_run = sum_bf16x2(pw[kb][ss].z, r_run);
+                r_run = sum_bf16x2(pw[kb][ss].w, r_run);
+            }
+        }
+        l_run += psum;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int ss = 0; ss < 2; ++ss) {
+                const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kb][ss]);
+                const int kbase_l = kb * 32 + 16 * ss + vkey_h + vrow_in;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const uint16_t* vp = Vt + kbase_l * VS + 32 * db + vcol_in;
+                    const s16x4 lo = lds_read_tr(vp);
+                    const s16x4 hi = lds_read_tr(vp + 8 * VS);
+                    const bf16x8 a = __builtin_bit_cast(
+                        bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
+                }
+            }
+        }
+        // K(t+2) replaces K(t), V(t+1) replaces V(t-1): both last read before
+        // the previous barrier
+        lstore(pk, Ks[t & 1], KS);
+        lstore(pv, Vs[(t + 1) & 1], VS);
         __syncthreads();
+        scur[0] = snext[0];
+        scur[1] = snext[1];
     }
 
     if (!active || qi >= Nq) return;
