@@ -8,7 +8,7 @@
 #include <cstdlib>
 #include <cstring>
 
-#include "../../include/attn.h"
+#include "attn.h"
 #include "launch.h"
 
 namespace {

@@ -207,7 +207,9 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     __syncthreads();
     qk(Ks[0], scur);
 
-    for (int t = 0; t < ntiles; ++t) {
+    // One tile iteration; the loop below alternates the two score buffers so
+    // no copy is needed between iterations.
+    auto step = [&](int t, f32x16 (&sc_)[2], f32x16 (&sn_)[2]) {
         const int key0 = t * kBc;
         // ---- short prologue (may branch): mask, row max, rare rescale
         const bool need_mask = (key0 + kBc > Nk) || (CAUSAL && key0 + kBc - 1 > wave_first);
@@ -219,7 +221,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                 for (int i = 0; i < 16; ++i) {
                     const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
                     const bool vis = (key < Nk) && (!CAUSAL || key <= qpos);
-                    scur[kb][i] = vis ? scur[kb][i] : -INFINITY;
+                    sc_[kb][i] = vis ? sc_[kb][i] : -INFINITY;
                 }
             }
         }
@@ -227,7 +229,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(scur[kb][i], scur[kb][i + 1]));
+            for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sc_[kb][i], sc_[kb][i + 1]));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_cand = mx * scale_log2;
         const bool grow = m_cand > m_run + kLazy;
@@ -247,7 +249,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         //      this tile's weights on the vector ALU, then P V.
         gload(pk, rk, key0 + 2 * kBc);  // K(t+2) in flight (zeros past the end)
         gload(pv, rv, key0 + kBc);      // V(t+1) in flight
-        qk(Ks[(t + 1) & 1], snext);
+        qk(Ks[(t + 1) & 1], sn_);
         const uint16_t* Vt = Vs[t & 1];
         float psum = 0.f;
         uint4 pw[2][2];
@@ -258,7 +260,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                 float p[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    p[e] = fast_exp2(fmaf(scur[kb][8 * ss + e], scale_log2, neg_m));
+                    p[e] = fast_exp2(fmaf(sc_[kb][8 * ss + e], scale_log2, neg_m));
                     psum += p[e];
                 }
                 pw[kb][ss].x = pack_bf16x2(p[0], p[1]);
@@ -294,9 +296,13 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         lstore(pk, Ks[t & 1], KS);
         lstore(pv, Vs[(t + 1) & 1], VS);
         __syncthreads();
-        scur[0] = snext[0];
-        scur[1] = snext[1];
+    };
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+        step(t, scur, snext);
+        step(t + 1, snext, scur);
     }
+    if (t < ntiles) step(t, scur, snext);
 
     if (!active || qi >= Nq) return;
     // O is the convex combination with the weights the MFMA actually used (their
