@@ -36,6 +36,39 @@ import workloads as W  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "exact_scaled_dot_amd", "csrc")
+
+
+def source_hash() -> str:
+    """Hash of the kernel sources, to tell whether recorded counters still apply."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of ``kernel`` from the committed counter record
+    (FETCH_SIZE and WRITE_SIZE, each scaled by the copy-kernel calibration), or
+    None when the record is missing or was taken on other kernel sources."""
+    try:
+        import json as _json
+        with open(TRAFFIC_RECORD) as f:
+            rec = _json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    cal = rec["calibration"]
+    return (k["fetch_kib"] * cal["fetch_factor"] + k["write_kib"] * cal["write_factor"]) * 1024.0
 METRIC = "attn fwd TFLOP/s (causal GQA N=8192 d=128 bf16) + decode HBM GB/s"
 
 
@@ -67,31 +100,37 @@ def dev(x):
     return torch.from_numpy(x).cuda()
 
 
-def cpu_baseline(w3, w4, budget_s=12.0):
-    """Time the fp64 oracle on bounded samples of both workloads on the host."""
+def cpu_baseline(w3, w4, budget_s=20.0):
+    """Time the fp64 oracle on bounded samples of both workloads on the host.
+
+    Prefill: whole query heads of the causal GQA N=8192 workload (all 8192 rows
+    of head 0, then head 1, ...) until half the budget is used; decode: whole
+    sequences of the decode workload until the other half is used.  The oracle
+    runs as it is (NumPy fp64, BLAS threads as configured on the host).
+    """
     import oracle.dense as oa
     try:
         from threadpoolctl import threadpool_info
         cores = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    # prefill sample: rows of head (0, 0), spread over the sequence
-    q, k, v = W.fwd_inputs(w3, B=1, Hq=1, Hkv=1)
-    rows_all = np.random.default_rng(0).permutation(w3.Nq)
+    q, k, v = W.fwd_inputs(w3)
     t0 = time.perf_counter()
-    done = 0
+    heads = 0
     pairs = 0
     kc = {}
-    while time.perf_counter() - t0 < budget_s * 0.5 and done < w3.Nq:
-        rows = np.sort(rows_all[done:done + 256])
-        oa.attention_rows(q, k, v, 0, 0, rows, causal=True, scale=w3.scale,
+    rows = np.arange(w3.Nq)
+    per_head_pairs = int(np.sum(rows + (w3.Nk - w3.Nq) + 1))
+    while time.perf_counter() - t0 < budget_s * 0.5 and heads < w3.B * w3.Hq:
+        b, h = divmod(heads, w3.Hq)
+        oa.attention_rows(q, k, v, b, h, rows, causal=True, scale=w3.scale,
                           rope_base=w3.rope_base, dtype="bf16", _kcache=kc)
-        pairs += int(np.sum(rows + (w3.Nk - w3.Nq) + 1))
-        done += len(rows)
+        pairs += per_head_pairs
+        heads += 1
     t_pf = time.perf_counter() - t0
     tflops = 4.0 * w3.d * pairs / t_pf / 1e12
-    # decode sample: full sequences of the decode workload, one after another
-    lens = W.decode_lens(w4)[:4]
+    del q, k, v
+    lens = W.decode_lens(w4)[:8]
     qd, kcache, vcache = W.decode_inputs(w4, lens, max_len=int(lens.max()))
     t0 = time.perf_counter()
     nb = 0
@@ -103,9 +142,10 @@ def cpu_baseline(w3, w4, budget_s=12.0):
     t_dec = time.perf_counter() - t0
     return {
         "value": tflops, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-        "sample": f"prefill: {done} query rows of head (0,0) of the causal GQA N=8192 workload "
-                  f"({t_pf:.1f} s, fp64 NumPy, RoPE + dense score rows); decode: {nb} full "
-                  f"sequences of the decode workload ({t_dec:.1f} s)",
+        "sample": f"prefill: {heads} whole query heads (8192 rows each) of the causal GQA RoPE "
+                  f"N=8192 workload in {t_pf:.1f} s (fp64 NumPy, RoPE rounding model, dense "
+                  f"score rows); decode: {nb} whole sequences of the decode workload in "
+                  f"{t_dec:.1f} s",
         "decode_value": nbytes / t_dec / 1e9, "decode_unit": "GB/s",
     }
 
@@ -118,7 +158,20 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="time one leg only (for profiling)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain 1 GiB device copy three times (counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = (1 << 30) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "copies": 3}))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
@@ -147,6 +200,7 @@ def main():
         l3 = torch.empty((w3.B, w3.Hq, w3.Nq), dtype=torch.float32, device="cuda")
         ws3 = torch.empty(esd.fwd_workspace_bytes(w3.B, w3.Hkv, w3.Nk, w3.d, w3.rope_base,
                                                   esd.ATTN_BF16), dtype=torch.uint8, device="cuda")
+        kr3 = torch.empty_like(dk)
     if do_dec:
         qd, kc, vc = W.decode_inputs(w4, lens)
         dqd, dkc, dvc, dlens = dev(qd), dev(kc), dev(vc), dev(lens)
@@ -163,6 +217,12 @@ def main():
             esd.fwd(dq, dk, dv, causal=True, scale=w3.scale, rope_base=w3.rope_base, out=o3, lse=l3,
                     workspace=ws3)
             if evs: evs[1].record(stream)
+            if evs:
+                # the same K rotation pass attn_fwd runs first, timed on its own so
+                # the attention kernel's share of the call is known
+                evs[4].record(stream)
+                esd.rope_apply(dk, w3.rope_base, 0, out=kr3)
+                evs[5].record(stream)
         if do_dec:
             if evs: evs[2].record(stream)
             esd.decode(dqd, dkc, dvc, dlens, scale=w4.scale, out=o4, lse=l4, workspace=ws4)
@@ -172,7 +232,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     print("[bench] timing", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -181,12 +241,23 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     pf_ms = [e[0].elapsed_time(e[1]) for e in evs] if do_pf else [float("nan")]
+    rope_ms = [e[4].elapsed_time(e[5]) for e in evs] if do_pf else [float("nan")]
     dec_ms = [e[2].elapsed_time(e[3]) for e in evs] if do_dec else [float("nan")]
     pf_avg = float(np.mean(pf_ms))
     dec_avg = float(np.mean(dec_ms))
 
+    rope_avg = float(np.mean(rope_ms))
     tflops = flops / (pf_avg * 1e-3) / 1e12 if do_pf else None
+    attn_ms = pf_avg - rope_avg
+    kern_tflops = flops / (attn_ms * 1e-3) / 1e12 if do_pf else None
     gbs = nbytes / (dec_avg * 1e-3) / 1e9 if do_dec else None
+    # the time of the step is the wall time; the K rotation timed separately is
+    # not part of it
+    wall -= float(np.sum(rope_ms)) * 1e-3 if do_pf else 0.0
+    pf_traffic = recorded_traffic("prefill_bf16_kernel<128, true, true>")
+    dec_split = recorded_traffic("decode_split_kernel<128, 4>")
+    dec_merge = recorded_traffic("decode_merge_kernel<128>")
+    dec_traffic = dec_split + dec_merge if dec_split is not None and dec_merge is not None else None
 
     rec = {
         "metric": METRIC,
@@ -205,17 +276,22 @@ def main():
             "workload": "prefill: causal GQA + RoPE 1e4, B=2 Hq=32 Hkv=8 N=8192 d=128 bf16; "
                         "decode: GQA B=32 Hq=32 Hkv=8 d=128 bf16, lens ~ U[1024,32768] seed 4004",
             "prefill_flops": flops, "prefill_ms": pf_avg, "prefill_ms_min": float(np.min(pf_ms)),
+            "prefill_rope_k_ms": rope_avg, "prefill_attention_kernel_ms": attn_ms,
             "decode_bytes": nbytes, "decode_ms": dec_avg, "decode_ms_min": float(np.min(dec_ms)),
         },
         "roofline": {
-            "bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": (tflops / PEAK_BF16_TFLOPS) if tflops else None, "traffic": None,
+            "kernel": "prefill_bf16_kernel<128, true, true>",
+            "bound": "mfma", "achieved": kern_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": (kern_tflops / PEAK_BF16_TFLOPS) if kern_tflops else None,
+            "traffic": pf_traffic,
         },
         "decode": {
             "value": gbs, "unit": "GB/s",
-            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": (gbs / PEAK_HBM_GBS) if gbs else None, "traffic": None},
+            "roofline": {"kernel": "decode_split_kernel<128, 4> + decode_merge_kernel<128>",
+                         "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": (gbs / PEAK_HBM_GBS) if gbs else None, "traffic": dec_traffic},
         },
+        "source_hash": source_hash(),
         "context": {
             "a100_roofline": "312 TFLOPS FP16, 1555 GB/s, ~200 FLOP/B",
             "materialised_scores_fp16_n8192_per_head_MB": 8192 * 8192 * 2 / 2 ** 20,
