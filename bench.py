@@ -150,6 +150,40 @@ def cpu_baseline(w3, w4, budget_s=20.0):
     }
 
 
+def extra_prefill(torch, esd, stream, reps=5):
+    """TFLOP/s of the other two prefill workloads (same entry point, same timing)."""
+    out = {}
+    for name in ("c2", "c5"):
+        w = W.WORKLOADS[name]
+        print(f"[bench] extra workload {name}: {w.note}", file=sys.stderr, flush=True)
+        q, k, v = W.fwd_inputs(w)
+        dq, dk, dv = dev(q), dev(k), dev(v)
+        del q, k, v
+        o = torch.empty((w.B, w.Hq, w.Nq, w.d), dtype=torch.float32, device="cuda")
+        lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
+        nws = esd.fwd_workspace_bytes(w.B, w.Hkv, w.Nk, w.d, w.rope_base, esd.ATTN_BF16)
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda") if nws else None
+        call = lambda: esd.fwd(dq, dk, dv, causal=w.causal, scale=w.scale, rope_base=w.rope_base,
+                               out=o, lse=lse, workspace=ws)
+        call()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            call()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        fl = fwd_flops(w)
+        out[name] = {"workload": w.note, "flops": fl, "ms": float(np.mean(ms)),
+                     "tflops": fl / (float(np.mean(ms)) * 1e-3) / 1e12}
+        del dq, dk, dv, o, lse, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,6 +192,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="time one leg only (for profiling)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the extra prefill workloads (MHA d=64 N=2048, GQA N=32768)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy three times (counter calibration)")
     args = ap.parse_args()
@@ -297,6 +333,11 @@ def main():
             "materialised_scores_fp16_n8192_per_head_MB": 8192 * 8192 * 2 / 2 ** 20,
         },
     }
+    if not args.no_extra and args.only is None:
+        # free the headline workloads' buffers before the long-context one
+        del dq, dk, dv, o3, l3, ws3, kr3, dqd, dkc, dvc, o4, l4, ws4
+        torch.cuda.empty_cache()
+        rec["extra"] = extra_prefill(torch, esd, stream)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(w3, w4)
