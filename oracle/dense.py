@@ -30,6 +30,10 @@ Readings where the pages are silent (each listed in the design notes):
   fp64 ``cos`` and ``sin`` (Python ``math``).
 * Query i sits at position Nk - Nq + i, key j at position j; causal visibility
   is j <= Nk - Nq + i.
+* Sliding window w ("Attention mechanisms: from alignment to efficient long
+  context", section 11): a key is visible when |p_q - p_k| < w, and in a causal
+  model also p_k <= p_q, so a causal query sees [p_q - w + 1, p_q].  w = 0
+  means no window.
 * logsumexp is the natural-log logsumexp of the visible scaled scores of a row.
 """
 
@@ -153,21 +157,28 @@ def _kv_head(h: int, Hq: int, Hkv: int) -> int:
     return h // (Hq // Hkv)
 
 
-def scores_and_weights(q_rows, k, *, scale, causal, q_pos, k_pos):
+def scores_and_weights(q_rows, k, *, scale, causal, q_pos, k_pos, window=0):
     """Scaled scores S (masked entries -inf) and softmax weights P for some rows.
 
     q_rows [r, d] at positions q_pos, k [n, d] at positions k_pos.  A key is
-    visible to a query when not causal or when its position is <= the query's.
+    visible to a query when not causal or when its position is <= the query's,
+    and, with a window w > 0, when the two positions differ by less than w.
     """
     s = (np.asarray(q_rows, np.float64) @ np.asarray(k, np.float64).T) * scale
+    kp = np.asarray(k_pos)[None, :]
+    qp = np.asarray(q_pos)[:, None]
+    vis = np.ones(s.shape, dtype=bool)
     if causal:
-        vis = np.asarray(k_pos)[None, :] <= np.asarray(q_pos)[:, None]
+        vis &= kp <= qp
+    if window:
+        vis &= np.abs(qp - kp) < window
+    if causal or window:
         s = np.where(vis, s, -np.inf)
     return s, softmax(s)
 
 
 def attention_rows(q, k, v, b: int, h: int, rows, *, causal: bool, scale: float,
-                   rope_base: float = 0.0, dtype: str = "bf16", _kcache=None):
+                   rope_base: float = 0.0, dtype: str = "bf16", window: int = 0, _kcache=None):
     """O [len(rows), d] and lse [len(rows)] for query rows of head (b, h).
 
     q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d]: fp32/fp64 arrays, or uint16 arrays of bf16
@@ -175,8 +186,8 @@ def attention_rows(q, k, v, b: int, h: int, rows, *, causal: bool, scale: float,
     """
     B, Hq, Nq, d = q.shape
     _, Hkv, Nk, _ = k.shape
-    if causal and Nq > Nk:
-        raise ValueError("causal attention needs Nq <= Nk")
+    if (causal or window) and Nq > Nk:
+        raise ValueError("causal or windowed attention needs Nq <= Nk")
     g = _kv_head(h, Hq, Hkv)
     rows = np.asarray(rows, dtype=np.int64)
     q_pos = rows + (Nk - Nq)
@@ -200,14 +211,14 @@ def attention_rows(q, k, v, b: int, h: int, rows, *, causal: bool, scale: float,
     for s0 in range(0, len(rows), panel):
         sl = slice(s0, s0 + panel)
         s, p = scores_and_weights(qr[sl], kg, scale=scale, causal=causal,
-                                  q_pos=q_pos[sl], k_pos=k_pos)
+                                  q_pos=q_pos[sl], k_pos=k_pos, window=window)
         o[sl] = p @ vg
         lse[sl] = logsumexp(s)
     return o, lse
 
 
 def attention(q, k, v, *, causal: bool, scale: float, rope_base: float = 0.0,
-              dtype: str = "bf16"):
+              dtype: str = "bf16", window: int = 0):
     """Full O [B,Hq,Nq,d] and lse [B,Hq,Nq] (fp64) for every head and row."""
     B, Hq, Nq, d = q.shape
     o = np.empty((B, Hq, Nq, d), dtype=np.float64)
@@ -217,7 +228,7 @@ def attention(q, k, v, *, causal: bool, scale: float, rope_base: float = 0.0,
         for h in range(Hq):
             o[b, h], lse[b, h] = attention_rows(
                 q, k, v, b, h, np.arange(Nq), causal=causal, scale=scale,
-                rope_base=rope_base, dtype=dtype, _kcache=kc)
+                rope_base=rope_base, dtype=dtype, window=window, _kcache=kc)
     return o, lse
 
 

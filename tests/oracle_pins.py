@@ -85,7 +85,7 @@ def _rot_complex(row, pos, base, dtype):
     return out
 
 
-def brute_attention(q, k, v, *, causal, scale, rope_base=0.0, dtype="f64"):
+def brute_attention(q, k, v, *, causal, scale, rope_base=0.0, dtype="f64", window=0):
     """Scalar-loop attention: for each query, exp-weights over visible keys.
 
     Visibility for t = Nq new queries over Nk keys follows [Scratch] 八 question 5
@@ -108,7 +108,12 @@ def brute_attention(q, k, v, *, causal, scale, rope_base=0.0, dtype="f64"):
                 pos = Nk - Nq + i
                 if rope_base:
                     qi = _rot_complex(qi, pos, rope_base, dtype)
-                vis = [j for j in range(Nk) if (not causal) or j <= pos]
+                if window and causal:    # [Evolution] section 11: keys pos-w+1 .. pos
+                    vis = list(range(max(0, pos - window + 1), pos + 1))
+                elif window:             # both sides: pos-w+1 .. pos+w-1
+                    vis = list(range(max(0, pos - window + 1), min(Nk, pos + window)))
+                else:
+                    vis = [j for j in range(Nk) if (not causal) or j <= pos]
                 s = {j: scale * sum(qi[t] * keys[j][t] for t in range(d)) for j in vis}
                 m = max(s.values())
                 w = {j: math.exp(s[j] - m) for j in vis}
@@ -351,6 +356,55 @@ def pin_lse_identity():
         vis = np.arange(14)[None, :] <= (np.arange(10) + 4)[:, None]
         tot = np.where(vis, np.exp(s - lse[0, h][:, None]), 0.0).sum(-1)
         assert np.max(np.abs(tot - 1)) < 1e-13
+
+
+_WINDOWED = [
+    # B, Hq, Hkv, Nq, Nk, d, causal, window, rope_base, dtype
+    (1, 2, 1, 9, 9, 8, True, 3, 0.0, "f64"),
+    (1, 4, 2, 6, 11, 8, True, 4, 100.0, "bf16"),
+    (2, 2, 2, 7, 7, 4, False, 2, 0.0, "f32"),
+    (1, 2, 1, 5, 12, 8, False, 5, 10.0, "bf16"),
+]
+
+
+def pin_window_brute_force_and_torch():
+    """Windowed attention = scalar loops over the key range [p-w+1, p] (causal)
+    or [p-w+1, p+w-1] ([Evolution] section 11), and = torch's fp64 SDPA with the
+    explicit mask |i - j| < w (and j <= i)."""
+    import torch
+    import torch.nn.functional as F
+    for n, (B, Hq, Hkv, Nq, Nk, d, causal, w, base, dt) in enumerate(_WINDOWED):
+        q, k, v = _rand_inputs(300 + n, B, Hq, Hkv, Nq, Nk, d, dt)
+        scale = 1.0 / math.sqrt(d)
+        o, lse = oa.attention(q, k, v, causal=causal, scale=scale, rope_base=base, dtype=dt, window=w)
+        ob, lb = brute_attention(q, k, v, causal=causal, scale=scale, rope_base=base, dtype=dt, window=w)
+        assert np.max(np.abs(o - ob)) < 1e-12 and np.max(np.abs(lse - lb)) < 1e-12, n
+        if base == 0.0:
+            i = np.arange(Nq)[:, None] + (Nk - Nq)
+            j = np.arange(Nk)[None, :]
+            mask = np.abs(i - j) < w
+            if causal:
+                mask &= j <= i
+            ot = F.scaled_dot_product_attention(
+                torch.tensor(q), torch.tensor(k), torch.tensor(v), attn_mask=torch.tensor(mask),
+                scale=scale, enable_gqa=True).numpy()
+            assert np.max(np.abs(o - ot)) < 1e-12, n
+
+
+def pin_window_special_cases():
+    """w = 1 (causal) leaves each query its own position: O_i = V[p_i] exactly and
+    lse_i = S[i, p_i]; a window at least as long as the keys changes nothing."""
+    B, Hq, Hkv, Nq, Nk, d = 1, 2, 1, 6, 10, 8
+    q, k, v = _rand_inputs(320, B, Hq, Hkv, Nq, Nk, d, "f64")
+    o, lse = oa.attention(q, k, v, causal=True, scale=0.4, dtype="f64", window=1)
+    for h in range(Hq):
+        for i in range(Nq):
+            p = Nk - Nq + i
+            assert np.all(o[0, h, i] == v[0, 0, p])
+            assert abs(lse[0, h, i] - 0.4 * np.dot(q[0, h, i], k[0, 0, p])) < 1e-13
+    o1, l1 = oa.attention(q, k, v, causal=True, scale=0.4, dtype="f64", window=Nk)
+    o2, l2 = oa.attention(q, k, v, causal=True, scale=0.4, dtype="f64")
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
 ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

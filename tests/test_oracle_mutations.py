@@ -19,11 +19,11 @@ _orig_rope = oa.rope
 _orig_lse = oa.logsumexp
 
 
-def _scores_no_scale(q_rows, k, *, scale, causal, q_pos, k_pos):
-    return _orig_scores(q_rows, k, scale=1.0, causal=causal, q_pos=q_pos, k_pos=k_pos)
+def _scores_no_scale(q_rows, k, *, scale, causal, q_pos, k_pos, window=0):
+    return _orig_scores(q_rows, k, scale=1.0, causal=causal, q_pos=q_pos, k_pos=k_pos, window=window)
 
 
-def _scores_strict(q_rows, k, *, scale, causal, q_pos, k_pos):
+def _scores_strict(q_rows, k, *, scale, causal, q_pos, k_pos, window=0):
     # mask off by one: j < i instead of j <= i (the diagonal hidden)
     s = (np.asarray(q_rows) @ np.asarray(k).T) * scale
     if causal:
@@ -33,13 +33,13 @@ def _scores_strict(q_rows, k, *, scale, causal, q_pos, k_pos):
         return s, oa.softmax(s)
 
 
-def _scores_top_left(q_rows, k, *, scale, causal, q_pos, k_pos):
+def _scores_top_left(q_rows, k, *, scale, causal, q_pos, k_pos, window=0):
     # causal aligned at the top-left corner instead of the bottom-right
     q_pos = np.asarray(q_pos) - (np.asarray(q_pos).min() if len(q_pos) else 0)
-    return _orig_scores(q_rows, k, scale=scale, causal=causal, q_pos=q_pos, k_pos=k_pos)
+    return _orig_scores(q_rows, k, scale=scale, causal=causal, q_pos=q_pos, k_pos=k_pos, window=window)
 
 
-def _scores_transposed(q_rows, k, *, scale, causal, q_pos, k_pos):
+def _scores_transposed(q_rows, k, *, scale, causal, q_pos, k_pos, window=0):
     s = (np.asarray(q_rows) @ np.asarray(k).T) * scale
     if s.shape[0] == s.shape[1]:
         s = s.T.copy()
@@ -108,7 +108,14 @@ def _round_truncate(x, dtype):
     return u.view(np.float32).astype(np.float64)
 
 
+def _scores_window_le(q_rows, k, *, scale, causal, q_pos, k_pos, window=0):
+    # window off by one: |i - j| <= w instead of < w
+    return _orig_scores(q_rows, k, scale=scale, causal=causal, q_pos=q_pos, k_pos=k_pos,
+                        window=window + 1 if window else 0)
+
+
 MUTATIONS = {
+    "window_off_by_one": ("scores_and_weights", _scores_window_le),
     "dropped_scale": ("scores_and_weights", _scores_no_scale),
     "mask_off_by_one": ("scores_and_weights", _scores_strict),
     "causal_top_left": ("scores_and_weights", _scores_top_left),
