@@ -72,16 +72,19 @@ def recorded_traffic(kernel: str):
 METRIC = "attn fwd TFLOP/s (causal GQA N=8192 d=128 bf16) + decode HBM GB/s"
 
 
-def visible_pairs(Nq, Nk, causal):
+def visible_pairs(Nq, Nk, causal, window=0):
     if not causal:
         return Nq * Nk
     off = Nk - Nq
+    if window:
+        # query i (position off+i) sees keys max(0, off+i-w+1) .. off+i
+        return int(np.minimum(np.arange(Nq, dtype=np.int64) + off + 1, window).sum())
     # query i sees keys 0..off+i
     return Nq * (off + 1) + Nq * (Nq - 1) // 2
 
 
-def fwd_flops(w):
-    return 4.0 * w.d * visible_pairs(w.Nq, w.Nk, w.causal) * w.B * w.Hq
+def fwd_flops(w, window=0):
+    return 4.0 * w.d * visible_pairs(w.Nq, w.Nk, w.causal, window) * w.B * w.Hq
 
 
 def decode_bytes(w, lens):
@@ -150,12 +153,19 @@ def cpu_baseline(w3, w4, budget_s=20.0):
     }
 
 
+EXTRA = (("c2", 0), ("c5", 0), ("c3", 4096), ("c5", 4096))
+
+
 def extra_prefill(torch, esd, stream, reps=5):
-    """TFLOP/s of the other two prefill workloads (same entry point, same timing)."""
+    """TFLOP/s of the other prefill workloads (same entry points, same timing):
+    MHA d=64 N=2048, long-context GQA N=32768, and the causal sliding window
+    (w=4096) on the GQA N=8192 and N=32768 shapes; flops count visible pairs."""
     out = {}
-    for name in ("c2", "c5"):
+    for name, win in EXTRA:
         w = W.WORKLOADS[name]
-        print(f"[bench] extra workload {name}: {w.note}", file=sys.stderr, flush=True)
+        label = f"{name}_w{win}" if win else name
+        note = f"{w.note}, sliding window {win}" if win else w.note
+        print(f"[bench] extra workload {label}: {note}", file=sys.stderr, flush=True)
         q, k, v = W.fwd_inputs(w)
         dq, dk, dv = dev(q), dev(k), dev(v)
         del q, k, v
@@ -164,7 +174,7 @@ def extra_prefill(torch, esd, stream, reps=5):
         nws = esd.fwd_workspace_bytes(w.B, w.Hkv, w.Nk, w.d, w.rope_base, esd.ATTN_BF16)
         ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda") if nws else None
         call = lambda: esd.fwd(dq, dk, dv, causal=w.causal, scale=w.scale, rope_base=w.rope_base,
-                               out=o, lse=lse, workspace=ws)
+                               out=o, lse=lse, workspace=ws, window=win)
         call()
         torch.cuda.synchronize()
         ms = []
@@ -176,8 +186,8 @@ def extra_prefill(torch, esd, stream, reps=5):
             b.record(stream)
             torch.cuda.synchronize()
             ms.append(a.elapsed_time(b))
-        fl = fwd_flops(w)
-        out[name] = {"workload": w.note, "flops": fl, "ms": float(np.mean(ms)),
+        fl = fwd_flops(w, win)
+        out[label] = {"workload": note, "flops": fl, "ms": float(np.mean(ms)),
                      "tflops": fl / (float(np.mean(ms)) * 1e-3) / 1e12}
         del dq, dk, dv, o, lse, ws
         torch.cuda.empty_cache()
@@ -193,7 +203,7 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="time one leg only (for profiling)")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the extra prefill workloads (MHA d=64 N=2048, GQA N=32768)")
+                    help="skip the extra prefill workloads (MHA d=64 N=2048, GQA N=32768, sliding window)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy three times (counter calibration)")
     args = ap.parse_args()

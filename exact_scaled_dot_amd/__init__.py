@@ -7,7 +7,8 @@ the GPU.  torch provides device memory and the current stream.  There is no
 fallback: if the library is missing, every call raises.
 
 Functions (same names as the C entry points):
-  fwd(q, k, v, causal, scale=None, rope_base=0.0, out=None, lse=None, workspace=None)
+  fwd(q, k, v, causal, scale=None, rope_base=0.0, out=None, lse=None, workspace=None,
+      window=0)       (window > 0: attn_fwd_window, causal sliding window)
   decode(q, k_cache, v_cache, seq_lens, scale=None, out=None, lse=None, workspace=None)
   rope_apply(x, rope_base, pos_offset=0, out=None)
   fwd_workspace_bytes(...), decode_workspace_bytes(...), status_str(code)
@@ -27,7 +28,7 @@ ATTN_F32 = 1
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_HIP",
           4: "ATTN_ERR_WORKSPACE"}
 
-EXPORTS = ("attn_status_str", "attn_fwd_workspace_bytes", "attn_fwd",
+EXPORTS = ("attn_status_str", "attn_fwd_workspace_bytes", "attn_fwd", "attn_fwd_window",
            "attn_decode_workspace_bytes", "attn_decode", "attn_rope_apply")
 
 _lib = None
@@ -55,6 +56,8 @@ def lib():
     L.attn_fwd_workspace_bytes.restype = sz
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, f, i, vp, sz, vp]
     L.attn_fwd.restype = i
+    L.attn_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, f, i, vp, sz, vp]
+    L.attn_fwd_window.restype = i
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
@@ -108,8 +111,11 @@ def decode_workspace_bytes(B, Hq, Hkv, max_len, d) -> int:
 
 
 def fwd(q, k, v, causal: bool, scale=None, rope_base: float = 0.0, out=None, lse=None,
-        workspace=None, want_lse: bool = True):
-    """O [B,Hq,Nq,d] fp32 and lse [B,Hq,Nq] fp32 of softmax(scale QK^T + M) V."""
+        workspace=None, want_lse: bool = True, window: int = 0):
+    """O [B,Hq,Nq,d] fp32 and lse [B,Hq,Nq] fp32 of softmax(scale QK^T + M) V.
+
+    window > 0 selects the causal sliding window (attn_fwd_window; causal must
+    then be true): the query at position p sees keys p-window+1 .. p."""
     import torch
     L = lib()
     for n, t in (("q", q), ("k", k), ("v", v)):
@@ -131,6 +137,13 @@ def fwd(q, k, v, causal: bool, scale=None, rope_base: float = 0.0, out=None, lse
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if window:
+        if not causal:
+            raise ValueError("the sliding window is causal: pass causal=True")
+        _check("attn_fwd_window", L.attn_fwd_window(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, int(window),
+            float(scale), float(rope_base), code, _ptr(workspace), wsb, _stream()))
+        return out, lse
     _check("attn_fwd", L.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv,
                                   Nq, Nk, d, int(bool(causal)), float(scale), float(rope_base),
                                   code, _ptr(workspace), wsb, _stream()))

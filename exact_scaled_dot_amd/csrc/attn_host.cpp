@@ -58,8 +58,13 @@ size_t attn_fwd_workspace_bytes(int B, int Hkv, int Nk, int d, float rope_base, 
     return (size_t)B * Hkv * Nk * d * elem_size(dtype);
 }
 
-int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
-             int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+}  // extern "C"
+
+namespace {
+
+// Shared body of attn_fwd (window = 0) and attn_fwd_window (window >= 1, causal).
+int fwd_impl(const void* q, const void* k, const void* v, float* o, float* lse,
+             int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int window,
              float scale, float rope_base, attn_dtype dtype,
              void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (B < 0 || Hq < 0 || Nq < 0) return fail(ATTN_ERR_INVALID, "negative size");
@@ -67,9 +72,12 @@ int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
     if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID, "Hq must be a multiple of Hkv");
     if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID, "causal must be 0 or 1");
     if (causal && Nq > Nk) return fail(ATTN_ERR_INVALID, "causal needs Nq <= Nk");
+    if (window < 0 || (window > 0 && !causal)) return fail(ATTN_ERR_INVALID, "window must be >= 1 and causal");
     if (!(std::isfinite(scale) && scale > 0.f)) return fail(ATTN_ERR_INVALID, "scale must be finite and > 0");
     if (rope_base != 0.f && !(std::isfinite(rope_base) && rope_base > 0.f))
         return fail(ATTN_ERR_INVALID, "rope_base must be 0 or a finite positive base");
+    if (rope_base != 0.f && Nq > Nk)
+        return fail(ATTN_ERR_INVALID, "RoPE needs Nq <= Nk (query positions Nk-Nq+i must be >= 0)");
     if (!known_dtype(dtype)) return fail(ATTN_ERR_INVALID, "unknown dtype");
     if (!supported_d(d)) return fail(ATTN_ERR_UNSUPPORTED, "head dim must be 64 or 128");
     if ((long long)Nk * d * 4 >= (1LL << 31))
@@ -88,6 +96,7 @@ int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.d = d;
     a.causal = causal; a.scale = scale; a.rope_tab = nullptr;
+    a.window = window < Nk ? window : 0;  // a window covering every key is plain causal
 
     if (rope) {
         int dev = 0;
@@ -111,6 +120,27 @@ int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
                                       : attn::launch_prefill_f32(a, stream);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, hipGetErrorString(e));
     return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
+             int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+             float scale, float rope_base, attn_dtype dtype,
+             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, 0, scale, rope_base, dtype,
+                    workspace, workspace_bytes, stream);
+}
+
+int attn_fwd_window(const void* q, const void* k, const void* v, float* o, float* lse,
+                    int B, int Hq, int Hkv, int Nq, int Nk, int d, int window,
+                    float scale, float rope_base, attn_dtype dtype,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (window < 1) return fail(ATTN_ERR_INVALID, "window must be >= 1");
+    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, 1, window, scale, rope_base, dtype,
+                    workspace, workspace_bytes, stream);
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int d) {

@@ -16,6 +16,7 @@ struct FwdArgs {
     float* lse;
     int B, Hq, Hkv, Nq, Nk, d;
     int causal;
+    int window;  // > 0: causal sliding window of this many keys; 0: none
     float scale;
     const double2* rope_tab;  // null: no RoPE on Q
 };

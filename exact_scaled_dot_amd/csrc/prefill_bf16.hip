@@ -37,6 +37,11 @@
 //   * causal: a workgroup stops at the last tile its rows can see, the element
 //     mask is applied only on tiles that cross a wave's diagonal or the end of
 //     K, and heavy row blocks are launched first.
+//   * sliding window w ("Attention mechanisms: from alignment to efficient long
+//     context", section 11; causal only): a query at position p sees keys
+//     p-w+1 .. p, so a workgroup also starts at the first tile its first row
+//     can see, and tiles that cross a wave's lower window edge are masked too.
+//     Work per row is then O(w) instead of O(N).
 
 #include "device_common.h"
 #include "launch.h"
@@ -67,13 +72,14 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
         (__attribute__((address_space(3))) s16x4*)(p));
 }
 
-template <int D, bool CAUSAL, bool ROPE>
+template <int D, bool CAUSAL, bool ROPE, bool WINDOW>
 __global__ void __launch_bounds__(kWaves * 64, 1)
 prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, float* __restrict__ o,
                     float* __restrict__ lse, int B, int Hq, int Hkv, int Nq, int Nk,
                     float scale_log2, const double2* __restrict__ tab, int hpw, int wph,
-                    int nchunks, int nrb) {
+                    int nchunks, int nrb, int win) {
+    static_assert(!WINDOW || CAUSAL, "the sliding window is built for causal attention");
     constexpr int NT = kWaves * 64;
     constexpr int KS = D + kKPad;       // K row stride in LDS (elements)
     constexpr int VS = D + kVPad;       // V row stride in LDS (elements)
@@ -114,9 +120,12 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
     int kend = Nk;
     if (CAUSAL) kend = min(Nk, off + min(Nq, row0 + wph * kRows));
-    const int ntiles = (kend + kBc - 1) / kBc;
+    // window: the first key any row of the workgroup sees, rounded down to a tile
+    const int kbeg = WINDOW ? max(0, off + row0 - win + 1) / kBc * kBc : 0;
+    const int ntiles = (kend - kbeg + kBc - 1) / kBc;
     const int wave_first = off + wrow0;                          // first row's position
     const int wave_last = off + min(Nq - 1, wrow0 + kRows - 1);  // last key this wave may see
+    const int wave_lo = wave_last - win + 1;  // window: keys below this are hidden from some row
 
     const uint16_t* kbase = k + ((size_t)b * Hkv + g) * (size_t)Nk * D;
     const uint16_t* vbase = v + ((size_t)b * Hkv + g) * (size_t)Nk * D;
@@ -150,8 +159,8 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         }
     };
 
-    gload(pk, rk, 0);
-    gload(pv, rv, 0);
+    gload(pk, rk, kbeg);
+    gload(pv, rv, kbeg);
 
     // ---- Q fragment (B operand of S^T = K Q^T): query l32, d = 16s + 8*half .. +7
     bf16x8 qf[D / 16];
@@ -202,7 +211,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     f32x16 scur[2], snext[2];
     lstore(pk, Ks[0], KS);
     lstore(pv, Vs[0], VS);
-    gload(pk, rk, kBc);
+    gload(pk, rk, kbeg + kBc);
     lstore(pk, Ks[1], KS);
     __syncthreads();
     qk(Ks[0], scur);
@@ -210,9 +219,10 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     // One tile iteration; the loop below alternates the two score buffers so
     // no copy is needed between iterations.
     auto step = [&](int t, f32x16 (&sc_)[2], f32x16 (&sn_)[2]) {
-        const int key0 = t * kBc;
+        const int key0 = kbeg + t * kBc;
         // ---- short prologue (may branch): mask, row max, rare rescale
-        const bool need_mask = (key0 + kBc > Nk) || (CAUSAL && key0 + kBc - 1 > wave_first);
+        const bool need_mask = (key0 + kBc > Nk) || (CAUSAL && key0 + kBc - 1 > wave_first) ||
+                               (WINDOW && key0 < wave_lo);
         if (need_mask) {
             keep_branch();
 #pragma unroll
@@ -220,7 +230,8 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-                    const bool vis = (key < Nk) && (!CAUSAL || key <= qpos);
+                    const bool vis = (key < Nk) && (!CAUSAL || key <= qpos) &&
+                                     (!WINDOW || key > qpos - win);
                     sc_[kb][i] = vis ? sc_[kb][i] : -INFINITY;
                 }
             }
@@ -325,7 +336,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         lse[((size_t)b * Hq + hq) * Nq + qi] = (m_run + fast_log2(l_tot)) * kLn2;
 }
 
-template <int D, bool CAUSAL, bool ROPE>
+template <int D, bool CAUSAL, bool ROPE, bool WINDOW>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     const int G = a.Hq / a.Hkv;
     const int hpw = G < kWaves ? G : kWaves;          // query heads per workgroup
@@ -337,18 +348,21 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     if (nwg == 0) return hipSuccess;
     if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
-    prefill_bf16_kernel<D, CAUSAL, ROPE><<<(unsigned)nwg, kWaves * 64, 0, stream>>>(
+    prefill_bf16_kernel<D, CAUSAL, ROPE, WINDOW><<<(unsigned)nwg, kWaves * 64, 0, stream>>>(
         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
         static_cast<const uint16_t*>(a.v), a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, scale_log2,
-        a.rope_tab, hpw, wph, nchunks, nrb);
+        a.rope_tab, hpw, wph, nchunks, nrb, WINDOW ? a.window : 0);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
     const bool rope = a.rope_tab != nullptr;
-    if (a.causal) return rope ? launch_t<D, true, true>(a, stream) : launch_t<D, true, false>(a, stream);
-    return rope ? launch_t<D, false, true>(a, stream) : launch_t<D, false, false>(a, stream);
+    if (a.window > 0)
+        return rope ? launch_t<D, true, true, true>(a, stream) : launch_t<D, true, false, true>(a, stream);
+    if (a.causal)
+        return rope ? launch_t<D, true, true, false>(a, stream) : launch_t<D, true, false, false>(a, stream);
+    return rope ? launch_t<D, false, true, false>(a, stream) : launch_t<D, false, false, false>(a, stream);
 }
 
 }  // namespace

@@ -4,7 +4,9 @@
 // "coding-interview attention from scratch", section 三.7), but one thread owns
 // one query row and every product is an fp32 FMA, so fp32 inputs keep fp32
 // precision end to end.  K/V tiles of 32 keys are shared by the 128 rows of a
-// workgroup through LDS; reads of a K or V row are LDS broadcasts.
+// workgroup through LDS; reads of a K or V row are LDS broadcasts.  With a
+// sliding window w (causal), the key loop starts at the first tile the
+// workgroup's first row can see and keys at or below position p-w are masked.
 
 #include "device_common.h"
 #include "launch.h"
@@ -16,12 +18,13 @@ namespace {
 constexpr int kRowsF = 128;  // query rows (threads) per workgroup
 constexpr int kBcF = 32;     // keys per tile
 
-template <int D, bool CAUSAL, bool ROPE>
+template <int D, bool CAUSAL, bool ROPE, bool WINDOW>
 __global__ void __launch_bounds__(kRowsF)
 prefill_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                    const float* __restrict__ v, float* __restrict__ o, float* __restrict__ lse,
                    int B, int Hq, int Hkv, int Nq, int Nk, float scale_log2,
-                   const double2* __restrict__ tab, int nrb) {
+                   const double2* __restrict__ tab, int nrb, int win) {
+    static_assert(!WINDOW || CAUSAL, "the sliding window is built for causal attention");
     __shared__ __attribute__((aligned(16))) float Ks[kBcF * D];
     __shared__ __attribute__((aligned(16))) float Vs[kBcF * D];
 
@@ -63,7 +66,8 @@ prefill_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
     const float* kbase = k + ((size_t)b * Hkv + g) * (size_t)Nk * D;
     const float* vbase = v + ((size_t)b * Hkv + g) * (size_t)Nk * D;
 
-    for (int key0 = 0; key0 < kend; key0 += kBcF) {
+    const int kbeg = WINDOW ? max(0, off + rb * kRowsF - win + 1) / kBcF * kBcF : 0;
+    for (int key0 = kbeg; key0 < kend; key0 += kBcF) {
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < (kBcF * D / 4) / kRowsF; ++i) {
@@ -88,7 +92,7 @@ prefill_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
 #pragma unroll
             for (int d = 0; d < D; ++d) a = fmaf(qv[d], Ks[j * D + d], a);
             const int key = key0 + j;
-            const bool vis = key < Nk && (!CAUSAL || key <= qpos);
+            const bool vis = key < Nk && (!CAUSAL || key <= qpos) && (!WINDOW || key > qpos - win);
             s[j] = vis ? a * scale_log2 : -INFINITY;
             mx = fmaxf(mx, s[j]);
         }
@@ -121,25 +125,28 @@ prefill_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
     if (lse != nullptr) lse[((size_t)b * Hq + hq) * Nq + qi] = (m_run + fast_log2(l_run)) * kLn2;
 }
 
-template <int D, bool CAUSAL, bool ROPE>
+template <int D, bool CAUSAL, bool ROPE, bool WINDOW>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     const int nrb = (a.Nq + kRowsF - 1) / kRowsF;
     const long long nwg = (long long)nrb * a.B * a.Hq;
     if (nwg == 0) return hipSuccess;
     if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
-    prefill_f32_kernel<D, CAUSAL, ROPE><<<(unsigned)nwg, kRowsF, 0, stream>>>(
+    prefill_f32_kernel<D, CAUSAL, ROPE, WINDOW><<<(unsigned)nwg, kRowsF, 0, stream>>>(
         static_cast<const float*>(a.q), static_cast<const float*>(a.k),
         static_cast<const float*>(a.v), a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, scale_log2,
-        a.rope_tab, nrb);
+        a.rope_tab, nrb, WINDOW ? a.window : 0);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
     const bool rope = a.rope_tab != nullptr;
-    if (a.causal) return rope ? launch_t<D, true, true>(a, stream) : launch_t<D, true, false>(a, stream);
-    return rope ? launch_t<D, false, true>(a, stream) : launch_t<D, false, false>(a, stream);
+    if (a.window > 0)
+        return rope ? launch_t<D, true, true, true>(a, stream) : launch_t<D, true, false, true>(a, stream);
+    if (a.causal)
+        return rope ? launch_t<D, true, true, false>(a, stream) : launch_t<D, true, false, false>(a, stream);
+    return rope ? launch_t<D, false, true, false>(a, stream) : launch_t<D, false, false, false>(a, stream);
 }
 
 }  // namespace

@@ -59,8 +59,9 @@ typedef enum {
 typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_INVALID = 1,     /* bad argument: null pointer, negative size, Hq % Hkv,
-                                 causal with Nq > Nk, non-finite scale, misaligned
-                                 pointer (16 bytes needed), scale <= 0 ... */
+                                 causal, windowed or RoPE call with Nq > Nk,
+                                 non-finite scale, misaligned pointer (16 bytes
+                                 needed), scale <= 0, window < 1 ... */
     ATTN_ERR_UNSUPPORTED = 2, /* valid but not built: d not in {64, 128}, f32 decode,
                                  a decode cache row range of 2 GiB or more */
     ATTN_ERR_HIP = 3,         /* a HIP call or kernel launch failed */
@@ -85,7 +86,8 @@ size_t attn_fwd_workspace_bytes(int B, int Hkv, int Nk, int d, float rope_base,
  *               Hkv >= 1, Hq % Hkv == 0, Nk >= 1, d in {64, 128}.
  *   causal      0 or 1.
  *   scale       finite multiplier of Q K^T, > 0 (1/sqrt(d) for standard attention).
- *   rope_base   0 = no RoPE, else a finite base > 0.
+ *   rope_base   0 = no RoPE, else a finite base > 0; RoPE needs Nq <= Nk
+ *               (query positions Nk - Nq + i are then >= 0).
  *   workspace   device buffer of attn_fwd_workspace_bytes(...) bytes (may be
  *               NULL when that is 0); holds the rotated K during the call.
  * All validation happens on the host before any HIP call.
@@ -94,6 +96,22 @@ int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
              int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
              float scale, float rope_base, attn_dtype dtype,
              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Causal sliding-window attention forward ("Attention mechanisms: from
+ * alignment to efficient long context", section 11): a query at position p
+ * sees the keys at positions p - window + 1 .. p (and never one past p), so
+ * each row costs O(window) instead of O(Nk).  Positions follow the causal
+ * bottom-right alignment above (query i at Nk - Nq + i).  Every row sees at
+ * least its own position, so no row is empty.
+ *   window      >= 1; a window of Nk or more keys equals attn_fwd(causal = 1).
+ *   Other arguments, layouts, workspace and errors as attn_fwd with causal = 1
+ *   (Nq <= Nk required).
+ */
+int attn_fwd_window(const void* q, const void* k, const void* v, float* o, float* lse,
+                    int B, int Hq, int Hkv, int Nq, int Nk, int d, int window,
+                    float scale, float rope_base, attn_dtype dtype,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace attn_decode needs for partial (max/sum, O) states. */
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int d);

@@ -130,6 +130,8 @@ def rope(x: np.ndarray, positions: np.ndarray, base: float, dtype: str) -> np.nd
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
     positions = np.asarray(positions, dtype=np.int64)
+    if positions.size and positions.min() < 0:
+        raise ValueError("RoPE positions start at 0")
     cos_t, sin_t = rope_cos_sin(int(positions.max()) + 1, d, base)
     c = cos_t[positions]
     s = sin_t[positions]
@@ -186,8 +188,9 @@ def attention_rows(q, k, v, b: int, h: int, rows, *, causal: bool, scale: float,
     """
     B, Hq, Nq, d = q.shape
     _, Hkv, Nk, _ = k.shape
-    if (causal or window) and Nq > Nk:
-        raise ValueError("causal or windowed attention needs Nq <= Nk")
+    if (causal or window or rope_base) and Nq > Nk:
+        # bottom-right positions Nk - Nq + i would be negative for the first rows
+        raise ValueError("causal, windowed or rotated attention needs Nq <= Nk")
     g = _kv_head(h, Hq, Hkv)
     rows = np.asarray(rows, dtype=np.int64)
     q_pos = rows + (Nk - Nq)

@@ -65,9 +65,31 @@ def _fwd(**kw):
     (dict(rope=-1.0), 1), (dict(rope=float("inf")), 1), (dict(dtype=7), 1),
     (dict(d=96), 2), (dict(d=32), 2), (dict(q=ctypes.c_void_p(258)), 1),
     (dict(rope=10000.0), 4), (dict(rope=10000.0, ws=P, wsb=100), 4),
+    (dict(causal=0, Nq=9, Nk=8, rope=100.0, ws=P, wsb=1 << 20), 1),  # negative RoPE positions
 ])
 def test_fwd_rejects_on_host(kw, code):
     assert _fwd(**kw) == code
+
+
+def _fwd_window(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Hq=4, Hkv=2, Nq=8, Nk=8, d=64, window=4,
+             scale=0.125, rope=0.0, dtype=esd.ATTN_BF16, ws=None, wsb=0)
+    a.update(kw)
+    return esd.lib().attn_fwd_window(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                                     a["Hkv"], a["Nq"], a["Nk"], a["d"], a["window"], a["scale"],
+                                     a["rope"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=0), 1), (dict(window=-3), 1), (dict(Nq=9, Nk=8), 1), (dict(v=None), 1),
+    (dict(d=80), 2), (dict(scale=0.0), 1), (dict(rope=100.0), 4),
+])
+def test_fwd_window_rejects_on_host(kw, code):
+    assert _fwd_window(**kw) == code
+
+
+def test_fwd_window_empty_is_a_noop():
+    assert _fwd_window(q=None, k=None, v=None, o=None, Nq=0) == 0
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(Hq=0, Hkv=1), dict(Nq=0)])
