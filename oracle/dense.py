@@ -258,3 +258,42 @@ def decode(q, k_cache, v_cache, seq_lens, *, scale: float):
             o[b, h] = p @ _f64(v_cache[b, g, :n])
             lse[b, h] = logsumexp(s)
     return o, lse
+
+
+def decode_multi(q, k_cache, v_cache, seq_lens, *, scale: float, rope_base: float = 0.0,
+                 dtype: str = "bf16"):
+    """T new queries per sequence over a contiguous cache.
+
+    "coding-interview attention from scratch", 八 question 5: with t new tokens
+    over len cached ones the score block is t x (len + t); the first len
+    columns are all visible and the last t form a lower triangle.  Here the
+    cache already holds the new tokens' K/V: sequence b has n = seq_lens[b]
+    rows, the last T of them new, so new token t sits at position n - T + t and
+    sees rows 0 .. n - T + t (the bottom-right causal rule).  Keys are stored
+    already rotated (三.6); with rope_base > 0 the query is rotated at its own
+    position and rounded to ``dtype``.  A token whose position is negative
+    (n < T) sees no key: O = 0 and lse = -inf, as for a length-0 decode.
+
+    q [B,Hq,T,d]; caches [B,Hkv,max_len,d]; returns O [B,Hq,T,d], lse [B,Hq,T].
+    """
+    B, Hq, T, d = q.shape
+    Hkv = k_cache.shape[1]
+    o = np.zeros((B, Hq, T, d), dtype=np.float64)
+    lse = np.full((B, Hq, T), -np.inf, dtype=np.float64)
+    for b in range(B):
+        n = int(seq_lens[b])
+        pos = np.arange(T) + (n - T)
+        rows = np.nonzero(pos >= 0)[0]
+        if len(rows) == 0:
+            continue
+        k_pos = np.arange(n)
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            qr = _f64(q[b, h, rows])
+            if rope_base:
+                qr = rope(qr, pos[rows], rope_base, dtype)
+            s, p = scores_and_weights(qr, _f64(k_cache[b, g, :n]), scale=scale, causal=True,
+                                      q_pos=pos[rows], k_pos=k_pos)
+            o[b, h, rows] = p @ _f64(v_cache[b, g, :n])
+            lse[b, h, rows] = logsumexp(s)
+    return o, lse

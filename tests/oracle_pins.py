@@ -407,4 +407,69 @@ def pin_window_special_cases():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+def _padded_cache(k, v, lens, max_len, seed):
+    """Caches [B,Hkv,max_len,d] holding k/v rows 0..lens[b]-1 and NaN after."""
+    B, Hkv, _, d = k.shape
+    kc = np.full((B, Hkv, max_len, d), np.nan)
+    vc = np.full((B, Hkv, max_len, d), np.nan)
+    for b, n in enumerate(lens):
+        kc[b, :, :n] = k[b, :, :n]
+        vc[b, :, :n] = v[b, :, :n]
+    return kc, vc
+
+
+def pin_decode_multi_against_page_mask():
+    """T new tokens over a cache: torch's fp64 SDPA with the mask built as
+    [Scratch] 八 question 5 states it, [all-True (T, len) | tril (T, T)], with
+    the query rotated by complex multiplication at position len + t; and scalar
+    loops (brute force) for the same rows."""
+    import torch
+    import torch.nn.functional as F
+    B, Hq, Hkv, T, d, max_len = 3, 4, 2, 5, 8, 24
+    lens = np.array([5, 12, 24])
+    for base, dt in ((0.0, "f64"), (100.0, "bf16")):
+        q, k, v = _rand_inputs(340 + int(base), B, Hq, Hkv, T, max_len, d, dt)
+        kc, vc = _padded_cache(k, v, lens, max_len, 0)
+        o, lse = oa.decode_multi(q, kc, vc, lens, scale=0.3, rope_base=base, dtype=dt)
+        for b, n in enumerate(lens):
+            hist = n - T
+            mask = np.concatenate([np.ones((T, hist), bool), np.tril(np.ones((T, T), bool))], axis=1)
+            qb = q[b].copy()
+            if base:
+                for h in range(Hq):
+                    for t in range(T):
+                        qb[h, t] = _rot_complex(list(q[b, h, t]), hist + t, base, dt)
+            ot = F.scaled_dot_product_attention(
+                torch.tensor(qb), torch.tensor(k[b, :, :n]), torch.tensor(v[b, :, :n]),
+                attn_mask=torch.tensor(mask), scale=0.3, enable_gqa=True).numpy()
+            assert np.max(np.abs(o[b] - ot)) < 1e-12, (b, base)
+            ob, lb = brute_attention(qb[None], k[b:b + 1, :, :n], v[b:b + 1, :, :n],
+                                     causal=True, scale=0.3, dtype="f64")
+            assert np.max(np.abs(o[b] - ob[0])) < 1e-12 and np.max(np.abs(lse[b] - lb[0])) < 1e-12
+
+
+def pin_decode_multi_incremental_and_short():
+    """Decoding the T tokens one at a time (cache prefix of n - T + t + 1 rows)
+    gives the same rows ([Scratch] 三.6: token-by-token decode = causal
+    attention); T = 1 is the single-query decode; a sequence with fewer than T
+    rows leaves its first tokens without keys (O = 0, lse = -inf)."""
+    B, Hq, Hkv, T, d, max_len = 2, 4, 1, 4, 8, 16
+    lens = np.array([2, 16])
+    q, k, v = _rand_inputs(360, B, Hq, Hkv, T, max_len, d, "f64")
+    kc, vc = _padded_cache(k, v, lens, max_len, 0)
+    o, lse = oa.decode_multi(q, kc, vc, lens, scale=0.5, dtype="f64")
+    for t in range(T):
+        n_t = np.maximum(lens - T + t + 1, 0)
+        od, ld = oa.decode(q[:, :, t], kc, vc, n_t, scale=0.5)
+        assert np.max(np.abs(od - o[:, :, t])) < 1e-14
+        assert np.array_equal(np.isneginf(ld), np.isneginf(lse[:, :, t]))
+        fin = np.isfinite(ld)
+        assert np.max(np.abs(ld[fin] - lse[:, :, t][fin])) < 1e-14
+    assert np.all(o[0, :, :2] == 0) and np.all(np.isneginf(lse[0, :, :2]))
+    assert np.all(np.isfinite(lse[0, :, 2:]))
+    o1, l1 = oa.decode_multi(q[:, :, :1], kc, vc, lens, scale=0.5, dtype="f64")
+    od, ld = oa.decode(q[:, :, 0], kc, vc, lens, scale=0.5)
+    assert np.array_equal(o1[:, :, 0], od) and np.array_equal(l1[:, :, 0], ld)
+
+
 ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

@@ -114,7 +114,16 @@ def _scores_window_le(q_rows, k, *, scale, causal, q_pos, k_pos, window=0):
                         window=window + 1 if window else 0)
 
 
+_orig_decode_multi = oa.decode_multi
+
+
+def _decode_multi_hides_self(q, k_cache, v_cache, seq_lens, **kw):
+    # each new token misses its own row: positions n - T + t - 1
+    return _orig_decode_multi(q, k_cache, v_cache, np.asarray(seq_lens) - 1, **kw)
+
+
 MUTATIONS = {
+    "decode_multi_hides_self": ("decode_multi", _decode_multi_hides_self),
     "window_off_by_one": ("scores_and_weights", _scores_window_le),
     "dropped_scale": ("scores_and_weights", _scores_no_scale),
     "mask_off_by_one": ("scores_and_weights", _scores_strict),
