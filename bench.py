@@ -87,11 +87,11 @@ def fwd_flops(w, window=0):
     return 4.0 * w.d * visible_pairs(w.Nq, w.Nk, w.causal, window) * w.B * w.Hq
 
 
-def decode_bytes(w, lens):
+def decode_bytes(w, lens, T=1):
     kv = int(np.sum(lens.astype(np.int64))) * w.Hkv * w.d * 2 * 2
-    q = w.B * w.Hq * w.d * 2
-    o = w.B * w.Hq * w.d * 4
-    lse = w.B * w.Hq * 4
+    q = w.B * w.Hq * T * w.d * 2
+    o = w.B * w.Hq * T * w.d * 4
+    lse = w.B * w.Hq * T * 4
     return kv + q + o + lse + w.B * 4
 
 
@@ -192,6 +192,32 @@ def extra_prefill(torch, esd, stream, reps=5):
         del dq, dk, dv, o, lse, ws
         torch.cuda.empty_cache()
     return out
+
+
+def extra_decode_multi(torch, esd, stream, w, lens, dkc, dvc, dlens, T=4, reps=10):
+    """GB/s of multi-token decode on the decode batch: T = 4 new tokens per
+    sequence (verifying drafted tokens), so 16 queries per KV head."""
+    print(f"[bench] extra workload decode_multi T={T}", file=sys.stderr, flush=True)
+    q = dev(W.normal((w.B, w.Hq, T, w.d), 9700, 1.0, "bf16"))
+    o = torch.empty((w.B, w.Hq, T, w.d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.Hq, T), dtype=torch.float32, device="cuda")
+    ws = torch.empty(esd.decode_multi_workspace_bytes(w.B, w.Hq, w.Hkv, T, w.max_len, w.d),
+                     dtype=torch.uint8, device="cuda")
+    call = lambda: esd.decode_multi(q, dkc, dvc, dlens, scale=w.scale, out=o, lse=lse, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    nb = decode_bytes(w, lens, T)
+    return {"workload": f"{w.note}, T={T} new tokens per sequence (bottom-right causal)",
+            "bytes": nb, "ms": float(np.mean(ms)), "gbs": nb / (float(np.mean(ms)) * 1e-3) / 1e9}
 
 
 def main():
@@ -344,6 +370,8 @@ def main():
         },
     }
     if not args.no_extra and args.only is None:
+        rec["extra_decode"] = {"decode_multi_T4": extra_decode_multi(torch, esd, stream, w4, lens,
+                                                                     dkc, dvc, dlens)}
         # free the headline workloads' buffers before the long-context one
         del dq, dk, dv, o3, l3, ws3, kr3, dqd, dkc, dvc, o4, l4, ws4
         torch.cuda.empty_cache()

@@ -10,8 +10,11 @@ Functions (same names as the C entry points):
   fwd(q, k, v, causal, scale=None, rope_base=0.0, out=None, lse=None, workspace=None,
       window=0)       (window > 0: attn_fwd_window, causal sliding window)
   decode(q, k_cache, v_cache, seq_lens, scale=None, out=None, lse=None, workspace=None)
+  decode_multi(q, k_cache, v_cache, seq_lens, scale=None, rope_base=0.0, out=None, lse=None,
+               workspace=None)   (q [B,Hq,T,d]: T new tokens per sequence)
   rope_apply(x, rope_base, pos_offset=0, out=None)
-  fwd_workspace_bytes(...), decode_workspace_bytes(...), status_str(code)
+  fwd_workspace_bytes(...), decode_workspace_bytes(...), decode_multi_workspace_bytes(...),
+  status_str(code)
 """
 
 from __future__ import annotations
@@ -29,7 +32,8 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID", 2: "ATTN_ERR_UNSUPPORTED", 3: "AT
           4: "ATTN_ERR_WORKSPACE"}
 
 EXPORTS = ("attn_status_str", "attn_fwd_workspace_bytes", "attn_fwd", "attn_fwd_window",
-           "attn_decode_workspace_bytes", "attn_decode", "attn_rope_apply")
+           "attn_decode_workspace_bytes", "attn_decode", "attn_decode_multi_workspace_bytes",
+           "attn_decode_multi", "attn_rope_apply")
 
 _lib = None
 
@@ -62,6 +66,10 @@ def lib():
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     L.attn_decode.restype = i
+    L.attn_decode_multi_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    L.attn_decode_multi_workspace_bytes.restype = sz
+    L.attn_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, i, vp, sz, vp]
+    L.attn_decode_multi.restype = i
     L.attn_rope_apply.argtypes = [vp, vp, i, i, i, i, i, f, i, vp]
     L.attn_rope_apply.restype = i
     _lib = L
@@ -108,6 +116,10 @@ def fwd_workspace_bytes(B, Hkv, Nk, d, rope_base, dtype_code) -> int:
 
 def decode_workspace_bytes(B, Hq, Hkv, max_len, d) -> int:
     return int(lib().attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d))
+
+
+def decode_multi_workspace_bytes(B, Hq, Hkv, T, max_len, d) -> int:
+    return int(lib().attn_decode_multi_workspace_bytes(B, Hq, Hkv, T, max_len, d))
 
 
 def fwd(q, k, v, causal: bool, scale=None, rope_base: float = 0.0, out=None, lse=None,
@@ -177,6 +189,37 @@ def decode(q, k_cache, v_cache, seq_lens, scale=None, out=None, lse=None, worksp
     _check("attn_decode", L.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
                                         _ptr(out), _ptr(lse), B, Hq, Hkv, max_len, d,
                                         float(scale), code, _ptr(workspace), wsb, _stream()))
+    return out, lse
+
+
+def decode_multi(q, k_cache, v_cache, seq_lens, scale=None, rope_base: float = 0.0, out=None,
+                 lse=None, workspace=None, want_lse: bool = True):
+    """T new tokens per sequence (q [B,Hq,T,d]); token t of sequence b sits at
+    position seq_lens[b] - T + t and sees cache rows up to that position."""
+    import torch
+    L = lib()
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
+        _need_cuda_contig(n, t)
+    if seq_lens.dtype != torch.int32:
+        raise TypeError("seq_lens must be int32")
+    B, Hq, T, d = q.shape
+    Bc, Hkv, max_len, dc = k_cache.shape
+    if (Bc, dc) != (B, d) or tuple(v_cache.shape) != tuple(k_cache.shape) or seq_lens.numel() != B:
+        raise ValueError("shape mismatch between q, caches and seq_lens")
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, T, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    need = decode_multi_workspace_bytes(B, Hq, Hkv, T, max_len, d)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("attn_decode_multi", L.attn_decode_multi(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(out), _ptr(lse), B, Hq, Hkv,
+        T, max_len, d, float(scale), float(rope_base), code, _ptr(workspace), wsb, _stream()))
     return out, lse
 
 

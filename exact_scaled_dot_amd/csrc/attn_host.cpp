@@ -143,34 +143,43 @@ int attn_fwd_window(const void* q, const void* k, const void* v, float* o, float
                     workspace, workspace_bytes, stream);
 }
 
-size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int d) {
-    if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_len <= 0 || d <= 0) return 0;
+size_t attn_decode_multi_workspace_bytes(int B, int Hq, int Hkv, int T, int max_len, int d) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0 || max_len <= 0 || d <= 0) return 0;
     const size_t nch = (size_t)(max_len + attn::kDecodeChunk - 1) / attn::kDecodeChunk;
-    const size_t rows = (size_t)B * Hq * nch;
+    const size_t rows = (size_t)B * Hq * T * nch;
     size_t o_bytes = rows * d * sizeof(float);
     o_bytes = (o_bytes + 255) & ~(size_t)255;
     return o_bytes + rows * sizeof(float);
 }
 
-int attn_decode(const void* q, const void* k_cache, const void* v_cache,
-                const int32_t* seq_lens, float* o, float* lse,
-                int B, int Hq, int Hkv, int max_len, int d, float scale,
-                attn_dtype dtype, void* workspace, size_t workspace_bytes,
-                hipStream_t stream) {
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int d) {
+    return attn_decode_multi_workspace_bytes(B, Hq, Hkv, 1, max_len, d);
+}
+
+int attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* seq_lens, float* o, float* lse,
+                      int B, int Hq, int Hkv, int T, int max_len, int d, float scale,
+                      float rope_base, attn_dtype dtype, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
     if (B < 0 || Hq < 0) return fail(ATTN_ERR_INVALID, "negative size");
-    if (Hkv < 1 || max_len < 1 || d < 1) return fail(ATTN_ERR_INVALID, "Hkv, max_len and d must be >= 1");
+    if (Hkv < 1 || T < 1 || max_len < 1 || d < 1)
+        return fail(ATTN_ERR_INVALID, "Hkv, T, max_len and d must be >= 1");
     if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID, "Hq must be a multiple of Hkv");
     if (!(std::isfinite(scale) && scale > 0.f)) return fail(ATTN_ERR_INVALID, "scale must be finite and > 0");
+    if (rope_base != 0.f && !(std::isfinite(rope_base) && rope_base > 0.f))
+        return fail(ATTN_ERR_INVALID, "rope_base must be 0 or a finite positive base");
     if (!known_dtype(dtype)) return fail(ATTN_ERR_INVALID, "unknown dtype");
     if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode is built for bf16");
     if (!supported_d(d)) return fail(ATTN_ERR_UNSUPPORTED, "head dim must be 64 or 128");
     if ((long long)max_len * d * 2 >= (1LL << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "one sequence's cache must be under 2 GiB (32-bit buffer offsets)");
+    if ((long long)B * Hq * T > 0x7fffffffLL)
+        return fail(ATTN_ERR_UNSUPPORTED, "B * Hq * T must fit in 31 bits");
     if (B == 0 || Hq == 0) return ATTN_OK;
     if (!q || !k_cache || !v_cache || !seq_lens || !o) return fail(ATTN_ERR_INVALID, "null pointer");
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
         return fail(ATTN_ERR_INVALID, "q, caches and o must be 16-byte aligned");
-    const size_t need = attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d);
+    const size_t need = attn_decode_multi_workspace_bytes(B, Hq, Hkv, T, max_len, d);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(ATTN_ERR_WORKSPACE, "decode workspace missing or too small");
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
@@ -182,15 +191,32 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
     a.v = static_cast<const uint16_t*>(v_cache);
     a.lens = seq_lens;
     a.o = o; a.lse = lse;
-    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.max_len = max_len; a.d = d; a.scale = scale;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.T = T; a.max_len = max_len; a.d = d; a.scale = scale;
+    a.rope_tab = nullptr;
+    if (rope_base > 0.f) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return fail(ATTN_ERR_HIP, "hipGetDevice");
+        a.rope_tab = attn::rope_table(dev, rope_base, d, max_len, &e);
+        if (!a.rope_tab) return fail(ATTN_ERR_HIP, "RoPE table");
+    }
     a.nchunks = (max_len + attn::kDecodeChunk - 1) / attn::kDecodeChunk;
-    const size_t rows = (size_t)B * Hq * a.nchunks;
+    const size_t rows = (size_t)B * Hq * T * a.nchunks;
     size_t o_bytes = (rows * d * sizeof(float) + 255) & ~(size_t)255;
     a.ws_o = static_cast<float*>(workspace);
     a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
     hipError_t e = attn::launch_decode_bf16(a, stream);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, hipGetErrorString(e));
     return ATTN_OK;
+}
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* seq_lens, float* o, float* lse,
+                int B, int Hq, int Hkv, int max_len, int d, float scale,
+                attn_dtype dtype, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+    return attn_decode_multi(q, k_cache, v_cache, seq_lens, o, lse, B, Hq, Hkv, 1, max_len, d,
+                             scale, 0.f, dtype, workspace, workspace_bytes, stream);
 }
 
 int attn_rope_apply(const void* x, void* out, int B, int H, int N, int d,

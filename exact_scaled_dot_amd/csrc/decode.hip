@@ -1,7 +1,11 @@
-// Decode: one query token per sequence against a contiguous KV cache.
+// Decode: T new query tokens per sequence against a contiguous KV cache.
 //
-// Each new query attends to every cached key with no mask ("coding-interview
-// attention from scratch", section 三.6).  Decode reads every cached K/V row
+// With T = 1 the new query attends to every cached key with no mask
+// ("coding-interview attention from scratch", section 三.6).  With T > 1 (the
+// same page, section 八 question 5: verifying several drafted tokens at once)
+// the cache already holds the new tokens' K/V and new token t, at position
+// len - T + t, sees cache rows 0 .. len - T + t: the whole history plus a lower
+// triangle over the new rows.  Decode reads every cached K/V row
 // once per step, so it is bound by memory bandwidth ("Transformer Architecture
 // Breakdown", Key Topic 3).  To spread one sequence over many compute units the
 // cache is split along its length: a split workgroup turns one chunk of keys
@@ -13,22 +17,25 @@
 //   M = max_c lse2_c,  w_c = 2^(lse2_c - M),  O = sum_c w_c O_c / sum_c w_c,
 //   lse = (M + log2 sum_c w_c) * ln 2.
 //
-// gfx950 mapping of the split kernel (one KV head, up to 16 query heads,
-// 1024 keys: 128 per wave, 8 waves):
+// gfx950 mapping of the split kernel (one KV head, up to 16 query columns,
+// 1024 keys: 128 per wave, 8 waves).  A column is one (query head, new token)
+// pair; the G*T columns of a KV head are G*T consecutive rows of q, so they
+// are numbered in that order and each keeps its own last visible key:
 //   * each wave streams its K rows and then its V rows in 32-key batches
 //     through a ring of four register slots (three batches always in flight,
 //     V loads start while the last K batches are in use); every load reads
 //     whole 256-byte rows and is unconditional, so the compiler keeps the
 //     batches in flight.
 //   * S = K q^T on v_mfma_f32_16x16x32_bf16 with the cached keys as rows and
-//     the group's query heads as columns, so each K row is read once for all
-//     heads that share it.  K rows go through a wave-private LDS slice; for
-//     MFMA step s the four lanes holding one key read its d range
-//     [32s, 32s + 32) there, and q uses the same d-slot order.  All scores of a wave stay in
-//     registers, so the per-head max is exact and nothing is rescaled.
-//   * V goes through a wave-private LDS slice and O = P V runs on the same MFMA: P (bf16) comes straight from the score
-//     registers as the A operand, the V operand is read with the transposing
-//     LDS load ds_read_b64_tr_b16.  O is normalised by the sum of the rounded
+//     the KV head's query columns as columns, so each K row is read once for
+//     all queries that share it.  K rows go through a wave-private LDS slice;
+//     for MFMA step s the four lanes holding one key read its d range
+//     [32s, 32s + 32) there, and q uses the same d-slot order.  All scores of a
+//     wave stay in registers, so the per-column max is exact and nothing is
+//     rescaled.
+//   * V goes through a wave-private LDS slice and O = P V runs on the same
+//     MFMA: P (bf16) comes straight from the score registers as the A operand,
+//     the V operand is read with the transposing LDS load ds_read_b64_tr_b16.  O is normalised by the sum of the rounded
 //     weights (v_dot2c_f32_bf16), the log-sum by the fp32 sum.
 //   * the eight waves' partial states are merged in LDS with the same rule the
 //     merge kernel uses, giving one partial state per 1024-key chunk.
@@ -65,14 +72,15 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D, int GP>
+template <int D, int GP, bool ROPE>
 __global__ void __launch_bounds__(kSplitWaves * 64)
 decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, const int32_t* __restrict__ lens,
                     float* __restrict__ ws_o, float* __restrict__ ws_lse, int B, int Hq,
-                    int Hkv, int max_len, float scale_log2, int nchunks, int nhch) {
+                    int Hkv, int T, int max_len, float scale_log2, int nchunks, int nhch,
+                    const double2* __restrict__ tab) {
     static_assert(D == 64 || D == 128, "head dim");
-    static_assert(GP >= 1 && GP <= 16, "heads per workgroup");
+    static_assert(GP >= 1 && GP <= 16, "columns per workgroup");
     constexpr int NS = D / 32;          // QK MFMA k-steps over d
     constexpr int NDB = D / 16;         // PV output blocks of 16 dims
     constexpr int VSD = D + 16;         // V row stride in LDS: 8 banks mod 64
@@ -99,19 +107,23 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const int g = idx % Hkv;
     const int b = idx / Hkv;
     const int G = Hq / Hkv;
-    const int h0 = g * G + hch * GP;             // first query head of this workgroup
-    const int nh = min(GP, G - hch * GP);        // heads handled here
+    const int NC = G * T;                        // columns of this KV head
+    const int f0 = hch * GP;                     // first column of this workgroup
+    const size_t row0 = ((size_t)b * Hq + (size_t)g * G) * T + f0;  // its q / output row
+    const int nh = min(GP, NC - f0);             // columns handled here
 
     int len = lens[b];
     len = len < 0 ? 0 : (len > max_len ? max_len : len);
     const int k0 = c * kCh;
     if (k0 >= len) return;
+    // last key visible to this lane's column (r16): its own position
+    const int lim = len - T + (f0 + min(r16, nh - 1)) % T;
 
     const size_t kvoff = ((size_t)b * Hkv + g) * (size_t)max_len * D;
     const uint16_t* kb = k + kvoff;
     const uint16_t* vb = v + kvoff;
-    const int wk0 = k0 + wave * kWaveKeys;             // first key of this wave
-    const int wn = max(0, min(kWaveKeys, len - wk0));  // keys of this wave
+    const int wk0 = k0 + wave * kWaveKeys;                   // first key of this wave
+    const int wn = max(0, min(kWaveKeys, lim + 1 - wk0));    // keys this column sees here
 
     // ---- one stream per wave: K batches 0..kNB-1, then V batches 0..kNB-1, each
     //      32 keys x D bf16 = VPL 16-byte pieces per lane, through a ring of
@@ -143,15 +155,19 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
     for (int e = 0; e < NSLOT - 1; ++e) sload(e, e);
 
-    // ---- q operand (B of S = K q^T): column r16 = head, d-slots 32s + 8*quarter ..
-    //      (columns past the last head read a valid head and are zeroed)
+    // ---- q operand (B of S = K q^T): column r16, d-slots 32s + 8*quarter ..
+    //      (columns past the last one read a valid row and are zeroed).  With
+    //      RoPE the query is rotated at its own position (cached keys are stored
+    //      rotated); a column without keys (lim < 0) uses position 0, unread.
     bf16x8 qf[NS];
     {
         const bool ok = r16 < nh;
-        const uint16_t* qrow = q + ((size_t)b * Hq + h0 + min(r16, nh - 1)) * D;
+        const uint16_t* qrow = q + (row0 + min(r16, nh - 1)) * D;
+        const double2* trow = ROPE ? tab + (size_t)max(lim, 0) * (D / 2) : nullptr;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             uint4 x = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * quarter);
+            if (ROPE) x = rope8_bf16(x, trow, 32 * s + 8 * quarter);
             if (!ok) x = make_uint4(0, 0, 0, 0);
             qf[s] = __builtin_bit_cast(bf16x8, x);
         }
@@ -257,7 +273,7 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         }
     }
 
-    // ---- merge the four waves' states in LDS
+    // ---- merge the eight waves' states in LDS
     if (quarter == 0) {
         cm[wave][r16] = m2;
         cl[wave][r16] = lsum;
@@ -281,37 +297,45 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         float acc = 0.f, rs = 0.f, ls = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            const float f = fast_exp2(cm[w][h] - M);  // 0 for a wave without keys
+            // 0 for a wave without keys for this column
+            const float f = cm[w][h] == -INFINITY ? 0.f : fast_exp2(cm[w][h] - M);
             acc = fmaf(f, co[w][h][d], acc);
             rs = fmaf(f, cr[w][h], rs);
             ls = fmaf(f, cl[w][h], ls);
         }
-        const size_t row = ((size_t)b * Hq + h0 + h) * nchunks + c;
-        ws_o[row * D + d] = acc / rs;
-        if (d == 0) ws_lse[row] = M + fast_log2(ls);
+        // a column with no key in this chunk (a new token before it) gets the
+        // empty state; the merge kernel never reads it
+        const bool empty = M == -INFINITY;
+        const size_t row = (row0 + h) * nchunks + c;
+        ws_o[row * D + d] = empty ? 0.f : acc / rs;
+        if (d == 0) ws_lse[row] = empty ? -INFINITY : M + fast_log2(ls);
     }
 }
 
-// One workgroup (256 threads) per (sequence, query head).  The chunk weights
-// w_c = 2^(lse2_c - M) are formed in parallel over chunks; then thread t sums
-// dim t % D over every (256 / D)-th chunk and the partial sums meet in LDS.
+// One workgroup (256 threads) per output row (sequence, query head, new
+// token).  Only the chunks holding keys the row can see are merged.  The chunk
+// weights w_c = 2^(lse2_c - M) are formed in parallel over chunks; then thread
+// t sums dim t % D over every (256 / D)-th chunk and the partial sums meet in
+// LDS.
 template <int D>
 __global__ void __launch_bounds__(256)
 decode_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
                     const int32_t* __restrict__ lens, float* __restrict__ o,
-                    float* __restrict__ lse, int Hq, int max_len, int nchunks) {
+                    float* __restrict__ lse, int Hq, int T, int max_len, int nchunks) {
     constexpr int NSPLIT = 256 / D;
     __shared__ float wts[1024];
     __shared__ float red[8];
     __shared__ float part[NSPLIT][D];
-    const int bh = blockIdx.x;
-    const int b = bh / Hq;
+    const int bh = blockIdx.x;  // output row
+    const int b = bh / (Hq * T);
+    const int t = bh % T;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     int len = lens[b];
     len = len < 0 ? 0 : (len > max_len ? max_len : len);
-    const int nc = (len + kCh - 1) / kCh;
+    const int nvis = max(0, len - T + t + 1);  // keys 0 .. len-T+t
+    const int nc = (nvis + kCh - 1) / kCh;
     if (nc == 0) {  // no visible key: empty sum
         if (tid < D) o[(size_t)bh * D + tid] = 0.f;
         if (lse != nullptr && tid == 0) lse[bh] = -INFINITY;
@@ -369,31 +393,38 @@ decode_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
     }
 }
 
-template <int D, int GP>
+template <int D, int GP, bool ROPE>
 hipError_t launch_split(const DecodeArgs& a, float scale_log2, hipStream_t stream) {
-    const int G = a.Hq / a.Hkv;
-    const int nhch = (G + GP - 1) / GP;
+    const long long NC = (long long)(a.Hq / a.Hkv) * a.T;
+    const long long nhch = (NC + GP - 1) / GP;
     const long long nwg = (long long)a.nchunks * nhch * a.Hkv * a.B;
     if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    decode_split_kernel<D, GP><<<(unsigned)nwg, kSplitWaves * 64, 0, stream>>>(
-        a.q, a.k, a.v, a.lens, a.ws_o, a.ws_lse, a.B, a.Hq, a.Hkv, a.max_len, scale_log2,
-        a.nchunks, nhch);
+    decode_split_kernel<D, GP, ROPE><<<(unsigned)nwg, kSplitWaves * 64, 0, stream>>>(
+        a.q, a.k, a.v, a.lens, a.ws_o, a.ws_lse, a.B, a.Hq, a.Hkv, a.T, a.max_len, scale_log2,
+        a.nchunks, (int)nhch, a.rope_tab);
     return hipGetLastError();
+}
+
+template <int D, bool ROPE>
+hipError_t launch_split_gp(const DecodeArgs& a, float scale_log2, hipStream_t stream) {
+    const long long NC = (long long)(a.Hq / a.Hkv) * a.T;  // columns per KV head
+    if (NC == 1) return launch_split<D, 1, ROPE>(a, scale_log2, stream);
+    if (NC == 2) return launch_split<D, 2, ROPE>(a, scale_log2, stream);
+    if (NC <= 4) return launch_split<D, 4, ROPE>(a, scale_log2, stream);
+    if (NC <= 8) return launch_split<D, 8, ROPE>(a, scale_log2, stream);
+    return launch_split<D, 16, ROPE>(a, scale_log2, stream);
 }
 
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
-    const int G = a.Hq / a.Hkv;
-    hipError_t e;
-    if (G == 1) e = launch_split<D, 1>(a, scale_log2, stream);
-    else if (G == 2) e = launch_split<D, 2>(a, scale_log2, stream);
-    else if (G <= 4) e = launch_split<D, 4>(a, scale_log2, stream);
-    else if (G <= 8) e = launch_split<D, 8>(a, scale_log2, stream);
-    else e = launch_split<D, 16>(a, scale_log2, stream);
+    const hipError_t e = a.rope_tab ? launch_split_gp<D, true>(a, scale_log2, stream)
+                                    : launch_split_gp<D, false>(a, scale_log2, stream);
     if (e != hipSuccess) return e;
-    decode_merge_kernel<D><<<(unsigned)(a.B * a.Hq), 256, 0, stream>>>(
-        a.ws_o, a.ws_lse, a.lens, a.o, a.lse, a.Hq, a.max_len, a.nchunks);
+    const long long rows = (long long)a.B * a.Hq * a.T;
+    if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    decode_merge_kernel<D><<<(unsigned)rows, 256, 0, stream>>>(
+        a.ws_o, a.ws_lse, a.lens, a.o, a.lse, a.Hq, a.T, a.max_len, a.nchunks);
     return hipGetLastError();
 }
 

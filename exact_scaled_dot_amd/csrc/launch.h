@@ -37,10 +37,11 @@ struct DecodeArgs {
     const int32_t* lens;
     float* o;
     float* lse;
-    int B, Hq, Hkv, max_len, d;
+    int B, Hq, Hkv, T, max_len, d;  // T new query tokens per sequence
     float scale;
-    float* ws_o;    // [B, Hq, nchunks, d]
-    float* ws_lse;  // [B, Hq, nchunks] (log2 domain)
+    const double2* rope_tab;  // null: no RoPE on the queries
+    float* ws_o;    // [B, Hq, T, nchunks, d]
+    float* ws_lse;  // [B, Hq, T, nchunks] (log2 domain)
     int nchunks;
 };
 

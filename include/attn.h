@@ -138,6 +138,40 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 attn_dtype dtype, void* workspace, size_t workspace_bytes,
                 hipStream_t stream);
 
+/* Bytes of workspace attn_decode_multi needs: B*Hq*T*ceil(max_len/1024)
+ * partial states of d + 1 floats (256-byte aligned split). */
+size_t attn_decode_multi_workspace_bytes(int B, int Hq, int Hkv, int T, int max_len, int d);
+
+/*
+ * Multi-token decode: T new query tokens per sequence against a contiguous KV
+ * cache that already holds their K/V, as when several drafted tokens are
+ * verified at once ("coding-interview attention from scratch", section 八
+ * question 5: the t x (len + t) score block is all visible over the history and
+ * lower-triangular over the new tokens).  With n = seq_lens[b] (clamped to
+ * [0, max_len]) new token t sits at position n - T + t and sees cache rows
+ * 0 .. n - T + t; a token whose position is negative (n < T) sees no key and
+ * gets O = 0, lse = -inf.  T = 1 with rope_base = 0 is attn_decode.
+ *   q          device [B, Hq, T, d] bf16.
+ *   k_cache, v_cache  device [B, Hkv, max_len, d] bf16, keys stored already
+ *              rotated when RoPE is used; rows past seq_lens[b] are never read.
+ *   seq_lens   device int32 [B].
+ *   o          device fp32 [B, Hq, T, d];  lse  device fp32 [B, Hq, T] or NULL.
+ *   rope_base  0 = queries used as given, else each query is rotated at its
+ *              own position (fp64, rounded to bf16) as attn_fwd rotates Q.
+ *   workspace  device buffer of attn_decode_multi_workspace_bytes(...) bytes,
+ *              256-byte aligned.
+ * Every KV head's G*T queries (G = Hq / Hkv) share one read of the cache when
+ * G*T <= 16; larger G*T re-read it once per 16 queries (from cache memory when
+ * the rereads run together), so long chunks of new tokens belong to attn_fwd.
+ * dtype must be ATTN_BF16; limits and errors as attn_decode, and B*Hq*T must
+ * fit in 31 bits.
+ */
+int attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* seq_lens, float* o, float* lse,
+                      int B, int Hq, int Hkv, int T, int max_len, int d, float scale,
+                      float rope_base, attn_dtype dtype, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
 /*
  * RoPE on its own: out[b,h,n,:] = rotate(x[b,h,n,:], position pos_offset + n),
  * rounded to `dtype` exactly as attn_fwd rounds the rotated operands.

@@ -120,6 +120,38 @@ def test_decode_empty_is_a_noop():
     assert _dec(B=0, q=None, k=None, v=None, lens=None, o=None, ws=None, wsb=0) == 0
 
 
+def _decm(**kw):
+    a = dict(q=P, k=P, v=P, lens=P, o=P, lse=None, B=2, Hq=8, Hkv=2, T=4, max_len=64, d=128,
+             scale=0.1, rope=0.0, dtype=esd.ATTN_BF16, ws=P, wsb=1 << 20)
+    a.update(kw)
+    return esd.lib().attn_decode_multi(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"], a["B"],
+                                       a["Hq"], a["Hkv"], a["T"], a["max_len"], a["d"], a["scale"],
+                                       a["rope"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=0), 1), (dict(T=-2), 1), (dict(lens=None), 1), (dict(Hq=6, Hkv=4), 1),
+    (dict(scale=0.0), 1), (dict(rope=-5.0), 1), (dict(rope=float("nan")), 1),
+    (dict(dtype=esd.ATTN_F32), 2), (dict(d=96), 2), (dict(ws=None), 4), (dict(wsb=100), 4),
+    (dict(ws=ctypes.c_void_p(272)), 1), (dict(B=1 << 12, Hq=1 << 12, Hkv=1, T=1 << 8), 2),
+])
+def test_decode_multi_rejects_on_host(kw, code):
+    assert _decm(**kw) == code
+
+
+def test_decode_multi_workspace():
+    one = esd.decode_workspace_bytes(3, 8, 2, 5000, 128)
+    assert esd.decode_multi_workspace_bytes(3, 8, 2, 1, 5000, 128) == one
+    rows = 3 * 8 * 6 * 5  # B * Hq * T * chunks of 1024 keys
+    n = esd.decode_multi_workspace_bytes(3, 8, 2, 6, 5000, 128)
+    assert rows * 129 * 4 <= n < rows * 129 * 4 + 256
+    assert esd.decode_multi_workspace_bytes(3, 8, 2, 0, 5000, 128) == 0
+
+
+def test_decode_multi_empty_is_a_noop():
+    assert _decm(B=0, q=None, k=None, v=None, lens=None, o=None, ws=None, wsb=0) == 0
+
+
 def test_rope_apply_rejects_on_host():
     L = esd.lib()
     assert L.attn_rope_apply(P, P, 1, 1, 4, 7, 0, 100.0, esd.ATTN_BF16, None) == 1
