@@ -297,3 +297,39 @@ def decode_multi(q, k_cache, v_cache, seq_lens, *, scale: float, rope_base: floa
             o[b, h, rows] = p @ _f64(v_cache[b, g, :n])
             lse[b, h, rows] = logsumexp(s)
     return o, lse
+
+
+def gather_paged(pool, block_table, n: int, b: int, block_size: int):
+    """Logical cache rows 0..n-1 of sequence b from a paged pool.
+
+    "Attention mechanisms: from alignment to efficient long context", section
+    20: position p lives in physical block table[p // block_size] at offset
+    p % block_size; "Transformer Architecture Breakdown" (Paged Attention)
+    stores a block as kv_cache[phys, :, offset, :], i.e. the pool is
+    [num_blocks, Hkv, block_size, d].  Returns [Hkv, n, d] as float64.
+    """
+    pos = np.arange(n)
+    phys = np.asarray(block_table[b])[pos // block_size]
+    rows = pool[phys, :, pos % block_size]          # [n, Hkv, d]
+    return np.transpose(_f64(rows), (1, 0, 2))
+
+
+def decode_paged(q, k_pool, v_pool, block_table, seq_lens, *, block_size: int, scale: float,
+                 rope_base: float = 0.0, dtype: str = "bf16"):
+    """Multi-token decode over a paged KV cache.
+
+    The attention is that of ``decode_multi`` (PagedAttention changes where K/V
+    rows live, not the arithmetic: same section 20); each sequence's rows are
+    first gathered through its block table.  q [B,Hq,T,d]; pools
+    [num_blocks, Hkv, block_size, d]; block_table [B, max_blocks] int.
+    """
+    B, Hq, T, d = q.shape
+    Hkv = k_pool.shape[1]
+    n_max = max([int(n) for n in seq_lens] + [1])
+    kc = np.zeros((B, Hkv, n_max, d))
+    vc = np.zeros((B, Hkv, n_max, d))
+    for b in range(B):
+        n = int(seq_lens[b])
+        kc[b, :, :n] = gather_paged(k_pool, block_table, n, b, block_size)
+        vc[b, :, :n] = gather_paged(v_pool, block_table, n, b, block_size)
+    return decode_multi(q, kc, vc, seq_lens, scale=scale, rope_base=rope_base, dtype=dtype)

@@ -472,4 +472,50 @@ def pin_decode_multi_incremental_and_short():
     assert np.array_equal(o1[:, :, 0], od) and np.array_equal(l1[:, :, 0], ld)
 
 
+class _PagePool:
+    """The allocation procedure of [Evolution] section 20 and [Breakdown] Paged
+    Attention, written as loops: a free list of physical blocks, a table per
+    request that grows by one block whenever a position starts a new block,
+    and each token's K/V written at kv[phys, :, offset, :]."""
+
+    def __init__(self, num_blocks, block_size, Hkv, d, seed):
+        self.free = list(_rng(seed).permutation(num_blocks))
+        self.bs = block_size
+        self.k = np.full((num_blocks, Hkv, block_size, d), np.nan)
+        self.v = np.full((num_blocks, Hkv, block_size, d), np.nan)
+        self.tables = {}
+
+    def append_token(self, req, position, k_tok, v_tok):
+        table = self.tables.setdefault(req, [])
+        if position % self.bs == 0:
+            table.append(self.free.pop())
+        phys, off = table[position // self.bs], position % self.bs
+        self.k[phys, :, off, :] = k_tok
+        self.v[phys, :, off, :] = v_tok
+
+
+def pin_paged_decode_equals_contiguous():
+    """Tokens appended one by one into a shuffled block pool, then decoded
+    through the block table, give exactly the contiguous-cache result (the
+    attention arithmetic is unchanged, [Evolution] section 20), for block sizes
+    that split sequences at different points; unused pool slots hold NaN."""
+    B, Hq, Hkv, T, d, max_len = 3, 4, 2, 3, 8, 40
+    lens = np.array([1, 17, 40])
+    q, k, v = _rand_inputs(380, B, Hq, Hkv, T, max_len, d, "f64")
+    kc, vc = _padded_cache(k, v, lens, max_len, 0)
+    ref = oa.decode_multi(q, kc, vc, lens, scale=0.4, dtype="f64")
+    for bs in (1, 4, 16):
+        nblk = sum(-(-int(n) // bs) for n in lens) + 3
+        pool = _PagePool(nblk, bs, Hkv, d, 390 + bs)
+        for b, n in enumerate(lens):
+            for p in range(n):
+                pool.append_token(b, p, k[b, :, p], v[b, :, p])
+        mb = max(len(t) for t in pool.tables.values())
+        table = np.full((B, mb + 2), -1, dtype=np.int64)
+        for b, t in pool.tables.items():
+            table[b, :len(t)] = t
+        got = oa.decode_paged(q, pool.k, pool.v, table, lens, block_size=bs, scale=0.4, dtype="f64")
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]), bs
+
+
 ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

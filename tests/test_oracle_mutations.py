@@ -122,7 +122,19 @@ def _decode_multi_hides_self(q, k_cache, v_cache, seq_lens, **kw):
     return _orig_decode_multi(q, k_cache, v_cache, np.asarray(seq_lens) - 1, **kw)
 
 
+_orig_gather = oa.gather_paged
+
+
+def _gather_swapped(pool, block_table, n, b, block_size):
+    # block index and offset swapped: table[p % bs], offset p // bs
+    pos = np.arange(n)
+    phys = np.asarray(block_table[b])[np.minimum(pos % block_size, np.asarray(block_table).shape[1] - 1)]
+    rows = pool[phys, :, np.minimum(pos // block_size, pool.shape[2] - 1)]
+    return np.transpose(np.asarray(rows, np.float64), (1, 0, 2))
+
+
 MUTATIONS = {
+    "paged_index_swapped": ("gather_paged", _gather_swapped),
     "decode_multi_hides_self": ("decode_multi", _decode_multi_hides_self),
     "window_off_by_one": ("scores_and_weights", _scores_window_le),
     "dropped_scale": ("scores_and_weights", _scores_no_scale),
