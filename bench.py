@@ -220,6 +220,36 @@ def extra_decode_multi(torch, esd, stream, w, lens, dkc, dvc, dlens, T=4, reps=1
             "bytes": nb, "ms": float(np.mean(ms)), "gbs": nb / (float(np.mean(ms)) * 1e-3) / 1e9}
 
 
+def extra_decode_paged(torch, esd, stream, w, lens, reps=10):
+    """GB/s of single-token decode on the decode batch with its cache in
+    16-token blocks scattered over a pool (bytes as for the contiguous cache)."""
+    print("[bench] extra workload decode_paged bs=16", file=sys.stderr, flush=True)
+    q, kp, vp, table = W.paged_inputs(w, lens, block_size=16)
+    dq, dkp, dvp, dt, dl = dev(q), dev(kp), dev(vp), dev(table), dev(lens)
+    del q, kp, vp
+    o = torch.empty((w.B, w.Hq, 1, w.d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.Hq, 1), dtype=torch.float32, device="cuda")
+    ws = torch.empty(esd.decode_paged_workspace_bytes(w.B, w.Hq, w.Hkv, 1, table.shape[1], 16, w.d),
+                     dtype=torch.uint8, device="cuda")
+    call = lambda: esd.decode_paged(dq, dkp, dvp, dt, dl, scale=w.scale, out=o, lse=lse, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    nb = decode_bytes(w, lens) + table.size * 4
+    del dq, dkp, dvp, dt, dl, o, lse, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"{w.note}, paged cache in blocks of 16 tokens", "bytes": nb,
+            "ms": float(np.mean(ms)), "gbs": nb / (float(np.mean(ms)) * 1e-3) / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -372,8 +402,11 @@ def main():
     if not args.no_extra and args.only is None:
         rec["extra_decode"] = {"decode_multi_T4": extra_decode_multi(torch, esd, stream, w4, lens,
                                                                      dkc, dvc, dlens)}
+        del dkc, dvc
+        torch.cuda.empty_cache()
+        rec["extra_decode"]["decode_paged_bs16"] = extra_decode_paged(torch, esd, stream, w4, lens)
         # free the headline workloads' buffers before the long-context one
-        del dq, dk, dv, o3, l3, ws3, kr3, dqd, dkc, dvc, o4, l4, ws4
+        del dq, dk, dv, o3, l3, ws3, kr3, dqd, o4, l4, ws4
         torch.cuda.empty_cache()
         rec["extra"] = extra_prefill(torch, esd, stream)
     if not args.no_cpu_baseline:

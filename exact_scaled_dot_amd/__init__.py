@@ -12,9 +12,11 @@ Functions (same names as the C entry points):
   decode(q, k_cache, v_cache, seq_lens, scale=None, out=None, lse=None, workspace=None)
   decode_multi(q, k_cache, v_cache, seq_lens, scale=None, rope_base=0.0, out=None, lse=None,
                workspace=None)   (q [B,Hq,T,d]: T new tokens per sequence)
+  decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale=None, rope_base=0.0, out=None,
+               lse=None, workspace=None)   (pools [num_blocks, Hkv, block_size, d])
   rope_apply(x, rope_base, pos_offset=0, out=None)
   fwd_workspace_bytes(...), decode_workspace_bytes(...), decode_multi_workspace_bytes(...),
-  status_str(code)
+  decode_paged_workspace_bytes(...), status_str(code)
 """
 
 from __future__ import annotations
@@ -33,7 +35,8 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID", 2: "ATTN_ERR_UNSUPPORTED", 3: "AT
 
 EXPORTS = ("attn_status_str", "attn_fwd_workspace_bytes", "attn_fwd", "attn_fwd_window",
            "attn_decode_workspace_bytes", "attn_decode", "attn_decode_multi_workspace_bytes",
-           "attn_decode_multi", "attn_rope_apply")
+           "attn_decode_multi", "attn_decode_paged_workspace_bytes", "attn_decode_paged",
+           "attn_rope_apply")
 
 _lib = None
 
@@ -70,6 +73,11 @@ def lib():
     L.attn_decode_multi_workspace_bytes.restype = sz
     L.attn_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, i, vp, sz, vp]
     L.attn_decode_multi.restype = i
+    L.attn_decode_paged_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    L.attn_decode_paged_workspace_bytes.restype = sz
+    L.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, f, i,
+                                    vp, sz, vp]
+    L.attn_decode_paged.restype = i
     L.attn_rope_apply.argtypes = [vp, vp, i, i, i, i, i, f, i, vp]
     L.attn_rope_apply.restype = i
     _lib = L
@@ -220,6 +228,45 @@ def decode_multi(q, k_cache, v_cache, seq_lens, scale=None, rope_base: float = 0
     _check("attn_decode_multi", L.attn_decode_multi(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(out), _ptr(lse), B, Hq, Hkv,
         T, max_len, d, float(scale), float(rope_base), code, _ptr(workspace), wsb, _stream()))
+    return out, lse
+
+
+def decode_paged_workspace_bytes(B, Hq, Hkv, T, max_blocks, block_size, d) -> int:
+    return int(lib().attn_decode_paged_workspace_bytes(B, Hq, Hkv, T, max_blocks, block_size, d))
+
+
+def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale=None, rope_base: float = 0.0,
+                 out=None, lse=None, workspace=None, want_lse: bool = True):
+    """decode_multi over a paged cache: token p of sequence b is row p % block_size
+    of pool block block_table[b, p // block_size]."""
+    import torch
+    L = lib()
+    for n, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("block_table", block_table),
+                 ("seq_lens", seq_lens)):
+        _need_cuda_contig(n, t)
+    if seq_lens.dtype != torch.int32 or block_table.dtype != torch.int32:
+        raise TypeError("seq_lens and block_table must be int32")
+    B, Hq, T, d = q.shape
+    num_blocks, Hkv, block_size, dp = k_pool.shape
+    Bt, max_blocks = block_table.shape
+    if (dp != d or tuple(v_pool.shape) != tuple(k_pool.shape) or seq_lens.numel() != B
+            or Bt != B):
+        raise ValueError("shape mismatch between q, pools, block_table and seq_lens")
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, T, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    need = decode_paged_workspace_bytes(B, Hq, Hkv, T, max_blocks, block_size, d)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("attn_decode_paged", L.attn_decode_paged(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), _ptr(out),
+        _ptr(lse), B, Hq, Hkv, T, num_blocks, block_size, max_blocks, d, float(scale),
+        float(rope_base), code, _ptr(workspace), wsb, _stream()))
     return out, lse
 
 

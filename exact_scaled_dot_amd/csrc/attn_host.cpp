@@ -156,11 +156,26 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int d) {
     return attn_decode_multi_workspace_bytes(B, Hq, Hkv, 1, max_len, d);
 }
 
-int attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
-                      const int32_t* seq_lens, float* o, float* lse,
-                      int B, int Hq, int Hkv, int T, int max_len, int d, float scale,
-                      float rope_base, attn_dtype dtype, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
+size_t attn_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int T, int max_blocks,
+                                         int block_size, int d) {
+    if (max_blocks <= 0 || block_size <= 0) return 0;
+    const long long max_len = (long long)max_blocks * block_size;
+    if (max_len > 0x7fffffffLL) return 0;
+    return attn_decode_multi_workspace_bytes(B, Hq, Hkv, T, (int)max_len, d);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared body of the three decode entry points.  table == nullptr: contiguous
+// caches [B, Hkv, max_len, d]; otherwise pools [num_blocks, Hkv, block_size, d]
+// addressed through table [B, max_blocks] (max_len = max_blocks * block_size).
+int decode_impl(const void* q, const void* k, const void* v, const int32_t* table,
+                const int32_t* seq_lens, float* o, float* lse, int B, int Hq, int Hkv, int T,
+                int max_len, int num_blocks, int block_size, int max_blocks, int d, float scale,
+                float rope_base, attn_dtype dtype, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
     if (B < 0 || Hq < 0) return fail(ATTN_ERR_INVALID, "negative size");
     if (Hkv < 1 || T < 1 || max_len < 1 || d < 1)
         return fail(ATTN_ERR_INVALID, "Hkv, T, max_len and d must be >= 1");
@@ -176,8 +191,8 @@ int attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
     if ((long long)B * Hq * T > 0x7fffffffLL)
         return fail(ATTN_ERR_UNSUPPORTED, "B * Hq * T must fit in 31 bits");
     if (B == 0 || Hq == 0) return ATTN_OK;
-    if (!q || !k_cache || !v_cache || !seq_lens || !o) return fail(ATTN_ERR_INVALID, "null pointer");
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    if (!q || !k || !v || !seq_lens || !o) return fail(ATTN_ERR_INVALID, "null pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return fail(ATTN_ERR_INVALID, "q, caches and o must be 16-byte aligned");
     const size_t need = attn_decode_multi_workspace_bytes(B, Hq, Hkv, T, max_len, d);
     if (workspace == nullptr || workspace_bytes < need)
@@ -187,12 +202,17 @@ int attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
 
     attn::DecodeArgs a{};
     a.q = static_cast<const uint16_t*>(q);
-    a.k = static_cast<const uint16_t*>(k_cache);
-    a.v = static_cast<const uint16_t*>(v_cache);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
     a.lens = seq_lens;
     a.o = o; a.lse = lse;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.T = T; a.max_len = max_len; a.d = d; a.scale = scale;
     a.rope_tab = nullptr;
+    a.table = table;
+    a.max_blocks = max_blocks;
+    a.num_blocks = num_blocks;
+    a.block_log2 = 0;
+    while ((1 << a.block_log2) < block_size) ++a.block_log2;
     if (rope_base > 0.f) {
         int dev = 0;
         hipError_t e = hipGetDevice(&dev);
@@ -208,6 +228,36 @@ int attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
     hipError_t e = attn::launch_decode_bf16(a, stream);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, hipGetErrorString(e));
     return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* seq_lens, float* o, float* lse,
+                      int B, int Hq, int Hkv, int T, int max_len, int d, float scale,
+                      float rope_base, attn_dtype dtype, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+    return decode_impl(q, k_cache, v_cache, nullptr, seq_lens, o, lse, B, Hq, Hkv, T, max_len,
+                       0, 1, 0, d, scale, rope_base, dtype, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_table, const int32_t* seq_lens, float* o, float* lse,
+                      int B, int Hq, int Hkv, int T, int num_blocks, int block_size,
+                      int max_blocks, int d, float scale, float rope_base, attn_dtype dtype,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (num_blocks < 1 || max_blocks < 1)
+        return fail(ATTN_ERR_INVALID, "num_blocks and max_blocks must be >= 1");
+    if (block_size < 16 || block_size > 4096 || (block_size & (block_size - 1)) != 0)
+        return fail(ATTN_ERR_UNSUPPORTED, "block_size must be a power of two in [16, 4096]");
+    if ((long long)max_blocks * block_size > 0x7fffffffLL)
+        return fail(ATTN_ERR_UNSUPPORTED, "max_blocks * block_size must fit in 31 bits");
+    if (B > 0 && Hq > 0 && block_table == nullptr) return fail(ATTN_ERR_INVALID, "null block table");
+    return decode_impl(q, k_pool, v_pool, block_table, seq_lens, o, lse, B, Hq, Hkv, T,
+                       max_blocks * block_size, num_blocks, block_size, max_blocks, d, scale,
+                       rope_base, dtype, workspace, workspace_bytes, stream);
 }
 
 int attn_decode(const void* q, const void* k_cache, const void* v_cache,

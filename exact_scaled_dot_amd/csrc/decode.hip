@@ -39,6 +39,17 @@
 //     weights (v_dot2c_f32_bf16), the log-sum by the fp32 sum.
 //   * the eight waves' partial states are merged in LDS with the same rule the
 //     merge kernel uses, giving one partial state per 1024-key chunk.
+//   * paged cache ("Attention mechanisms: from alignment to efficient long
+//     context", section 20; "Transformer Architecture Breakdown", Paged
+//     Attention): the pools are [num_blocks, Hkv, block_size, d] and token p of
+//     sequence b lives in block table[b][p / block_size] at row p % block_size.
+//     One load instruction covers 4 (d = 128) or 8 (d = 64) consecutive keys,
+//     which never straddle a block of 16 or more rows, so each instruction gets
+//     a scalar buffer resource whose base is its block and whose size is the
+//     block's rows below the sequence length: rows past the end read as zeros,
+//     as in the contiguous case, and the loads stay unconditional.  A wave
+//     fetches its (at most eight) table entries once, one per lane, and picks
+//     each instruction's entry with v_readlane.
 
 #include "device_common.h"
 #include "launch.h"
@@ -72,13 +83,14 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D, int GP, bool ROPE>
+template <int D, int GP, bool PAGED>
 __global__ void __launch_bounds__(kSplitWaves * 64)
 decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, const int32_t* __restrict__ lens,
                     float* __restrict__ ws_o, float* __restrict__ ws_lse, int B, int Hq,
                     int Hkv, int T, int max_len, float scale_log2, int nchunks, int nhch,
-                    const double2* __restrict__ tab) {
+                    const double2* __restrict__ tab, const int32_t* __restrict__ table,
+                    int max_blocks, int lbs, int num_blocks) {
     static_assert(D == 64 || D == 128, "head dim");
     static_assert(GP >= 1 && GP <= 16, "columns per workgroup");
     constexpr int NS = D / 32;          // QK MFMA k-steps over d
@@ -91,7 +103,7 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     __shared__ float co[NW][GP][D];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int r16 = lane & 15;
     const int quarter = lane >> 4;
@@ -125,6 +137,16 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const int wk0 = k0 + wave * kWaveKeys;                   // first key of this wave
     const int wn = max(0, min(kWaveKeys, lim + 1 - wk0));    // keys this column sees here
 
+    // paged: lane i holds the physical block of this wave's i-th block of keys
+    // (indices past the sequence's last block repeat that block; entries are
+    // clamped into the pool)
+    int ent = 0;
+    if constexpr (PAGED) {
+        const int nblk = (len + (1 << lbs) - 1) >> lbs;  // >= 1: len > k0 >= 0
+        ent = table[(size_t)b * max_blocks + min((wk0 >> lbs) + lane, nblk - 1)];
+        ent = min(max(ent, 0), num_blocks - 1);
+    }
+
     // ---- one stream per wave: K batches 0..kNB-1, then V batches 0..kNB-1, each
     //      32 keys x D bf16 = VPL 16-byte pieces per lane, through a ring of
     //      NSLOT register slots, so NSLOT-1 batches are in flight (V loads start
@@ -145,12 +167,29 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(vb), (short)0, len * D * 2, 0x00020000);
     const int lane_off = (lane / (D / 8)) * D * 2 + (lane % (D / 8)) * 16;  // bytes
-    constexpr int JSTEP = 64 / (D / 8) * D * 2;                               // bytes per j
+    constexpr int KPJ = 64 / (D / 8);                                         // keys per j
+    constexpr int JSTEP = KPJ * D * 2;                                        // bytes per j
     auto sload = [&](int e, int slot) {
-        const int boff = (wk0 + kBatch * (e < kNB ? e : e - kNB)) * D * 2 + lane_off;
+        const int bi = e < kNB ? e : e - kNB;
+        if constexpr (PAGED) {
+            const uint16_t* pool = e < kNB ? k : v;
 #pragma unroll
-        for (int j = 0; j < VPL; ++j)
-            ring[slot][j] = __builtin_amdgcn_raw_buffer_load_b128(e < kNB ? rk : rv, boff + JSTEP * j, 0, 0);
+            for (int j = 0; j < VPL; ++j) {
+                const int key = wk0 + kBatch * bi + KPJ * j;  // first key of this load
+                const int ks = key & -(1 << lbs);             // first key of its block
+                const int phys = __builtin_amdgcn_readlane(ent, (key >> lbs) - (wk0 >> lbs));
+                const int nvalid = min(max(len - ks, 0), 1 << lbs);
+                const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<uint16_t*>(pool + ((size_t)phys * Hkv + g) * ((size_t)D << lbs)),
+                    (short)0, nvalid * D * 2, 0x00020000);
+                ring[slot][j] = __builtin_amdgcn_raw_buffer_load_b128(r, (key - ks) * D * 2 + lane_off, 0, 0);
+            }
+        } else {
+            const int boff = (wk0 + kBatch * bi) * D * 2 + lane_off;
+#pragma unroll
+            for (int j = 0; j < VPL; ++j)
+                ring[slot][j] = __builtin_amdgcn_raw_buffer_load_b128(e < kNB ? rk : rv, boff + JSTEP * j, 0, 0);
+        }
     };
 #pragma unroll
     for (int e = 0; e < NSLOT - 1; ++e) sload(e, e);
@@ -163,11 +202,11 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     {
         const bool ok = r16 < nh;
         const uint16_t* qrow = q + (row0 + min(r16, nh - 1)) * D;
-        const double2* trow = ROPE ? tab + (size_t)max(lim, 0) * (D / 2) : nullptr;
+        const double2* trow = tab + (size_t)max(lim, 0) * (D / 2);
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             uint4 x = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * quarter);
-            if (ROPE) x = rope8_bf16(x, trow, 32 * s + 8 * quarter);
+            if (tab != nullptr) x = rope8_bf16(x, trow, 32 * s + 8 * quarter);
             if (!ok) x = make_uint4(0, 0, 0, 0);
             qf[s] = __builtin_bit_cast(bf16x8, x);
         }
@@ -393,33 +432,33 @@ decode_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
     }
 }
 
-template <int D, int GP, bool ROPE>
+template <int D, int GP, bool PAGED>
 hipError_t launch_split(const DecodeArgs& a, float scale_log2, hipStream_t stream) {
     const long long NC = (long long)(a.Hq / a.Hkv) * a.T;
     const long long nhch = (NC + GP - 1) / GP;
     const long long nwg = (long long)a.nchunks * nhch * a.Hkv * a.B;
     if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    decode_split_kernel<D, GP, ROPE><<<(unsigned)nwg, kSplitWaves * 64, 0, stream>>>(
+    decode_split_kernel<D, GP, PAGED><<<(unsigned)nwg, kSplitWaves * 64, 0, stream>>>(
         a.q, a.k, a.v, a.lens, a.ws_o, a.ws_lse, a.B, a.Hq, a.Hkv, a.T, a.max_len, scale_log2,
-        a.nchunks, (int)nhch, a.rope_tab);
+        a.nchunks, (int)nhch, a.rope_tab, a.table, a.max_blocks, a.block_log2, a.num_blocks);
     return hipGetLastError();
 }
 
-template <int D, bool ROPE>
+template <int D, bool PAGED>
 hipError_t launch_split_gp(const DecodeArgs& a, float scale_log2, hipStream_t stream) {
     const long long NC = (long long)(a.Hq / a.Hkv) * a.T;  // columns per KV head
-    if (NC == 1) return launch_split<D, 1, ROPE>(a, scale_log2, stream);
-    if (NC == 2) return launch_split<D, 2, ROPE>(a, scale_log2, stream);
-    if (NC <= 4) return launch_split<D, 4, ROPE>(a, scale_log2, stream);
-    if (NC <= 8) return launch_split<D, 8, ROPE>(a, scale_log2, stream);
-    return launch_split<D, 16, ROPE>(a, scale_log2, stream);
+    if (NC == 1) return launch_split<D, 1, PAGED>(a, scale_log2, stream);
+    if (NC == 2) return launch_split<D, 2, PAGED>(a, scale_log2, stream);
+    if (NC <= 4) return launch_split<D, 4, PAGED>(a, scale_log2, stream);
+    if (NC <= 8) return launch_split<D, 8, PAGED>(a, scale_log2, stream);
+    return launch_split<D, 16, PAGED>(a, scale_log2, stream);
 }
 
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
-    const hipError_t e = a.rope_tab ? launch_split_gp<D, true>(a, scale_log2, stream)
-                                    : launch_split_gp<D, false>(a, scale_log2, stream);
+    const hipError_t e = a.table ? launch_split_gp<D, true>(a, scale_log2, stream)
+                                 : launch_split_gp<D, false>(a, scale_log2, stream);
     if (e != hipSuccess) return e;
     const long long rows = (long long)a.B * a.Hq * a.T;
     if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;

@@ -40,6 +40,10 @@ struct DecodeArgs {
     int B, Hq, Hkv, T, max_len, d;  // T new query tokens per sequence
     float scale;
     const double2* rope_tab;  // null: no RoPE on the queries
+    // paged cache (table != null): k, v are pools [num_blocks, Hkv, 2^block_log2, d],
+    // table [B, max_blocks]; max_len = max_blocks << block_log2
+    const int32_t* table;
+    int max_blocks, block_log2, num_blocks;
     float* ws_o;    // [B, Hq, T, nchunks, d]
     float* ws_lse;  // [B, Hq, T, nchunks] (log2 domain)
     int nchunks;

@@ -172,6 +172,39 @@ int attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
                       float rope_base, attn_dtype dtype, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of workspace attn_decode_paged needs: as attn_decode_multi with
+ * max_len = max_blocks * block_size (0 when that overflows). */
+size_t attn_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int T, int max_blocks,
+                                         int block_size, int d);
+
+/*
+ * Multi-token decode over a paged KV cache ("Attention mechanisms: from
+ * alignment to efficient long context", section 20; "Transformer Architecture
+ * Breakdown", Paged Attention).  The arithmetic is that of attn_decode_multi;
+ * only where the K/V rows live changes: token position p of sequence b is row
+ * p % block_size of physical block block_table[b * max_blocks + p / block_size].
+ *   q          device [B, Hq, T, d] bf16.
+ *   k_pool, v_pool  device [num_blocks, Hkv, block_size, d] bf16 (a block holds
+ *              block_size consecutive tokens of every KV head).
+ *   block_table  device int32 [B, max_blocks]; the entries for the blocks that
+ *              hold rows 0 .. seq_lens[b]-1 must name physical blocks (values
+ *              are clamped into [0, num_blocks) before use); later entries are
+ *              never used to read memory.
+ *   seq_lens   device int32 [B], clamped to [0, max_blocks * block_size].  Rows
+ *              at or past seq_lens[b] inside its last block are never read.
+ *   block_size power of two in [16, 4096] (16 is the usual choice).
+ *   o, lse, T, scale, rope_base, dtype, workspace: as attn_decode_multi, with
+ *              attn_decode_paged_workspace_bytes(...) bytes of workspace.
+ * Errors: num_blocks or max_blocks < 1, or a null table -> ATTN_ERR_INVALID;
+ * another block_size, or max_blocks * block_size * d * 2 >= 2^31 ->
+ * ATTN_ERR_UNSUPPORTED; otherwise as attn_decode_multi.
+ */
+int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_table, const int32_t* seq_lens, float* o, float* lse,
+                      int B, int Hq, int Hkv, int T, int num_blocks, int block_size,
+                      int max_blocks, int d, float scale, float rope_base, attn_dtype dtype,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /*
  * RoPE on its own: out[b,h,n,:] = rotate(x[b,h,n,:], position pos_offset + n),
  * rounded to `dtype` exactly as attn_fwd rounds the rotated operands.

@@ -148,6 +148,32 @@ def test_decode_multi_workspace():
     assert esd.decode_multi_workspace_bytes(3, 8, 2, 0, 5000, 128) == 0
 
 
+def _decp(**kw):
+    a = dict(q=P, k=P, v=P, table=P, lens=P, o=P, lse=None, B=2, Hq=8, Hkv=2, T=1, nblk=64,
+             bs=16, mb=8, d=128, scale=0.1, rope=0.0, dtype=esd.ATTN_BF16, ws=P, wsb=1 << 20)
+    a.update(kw)
+    return esd.lib().attn_decode_paged(a["q"], a["k"], a["v"], a["table"], a["lens"], a["o"],
+                                       a["lse"], a["B"], a["Hq"], a["Hkv"], a["T"], a["nblk"],
+                                       a["bs"], a["mb"], a["d"], a["scale"], a["rope"], a["dtype"],
+                                       a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(table=None), 1), (dict(nblk=0), 1), (dict(mb=0), 1), (dict(bs=8), 2), (dict(bs=24), 2),
+    (dict(bs=8192), 2), (dict(mb=1 << 20, bs=4096), 2), (dict(T=0), 1), (dict(lens=None), 1),
+    (dict(dtype=esd.ATTN_F32), 2), (dict(ws=None), 4), (dict(d=80), 2),
+])
+def test_decode_paged_rejects_on_host(kw, code):
+    assert _decp(**kw) == code
+
+
+def test_decode_paged_workspace_and_noop():
+    assert (esd.decode_paged_workspace_bytes(3, 8, 2, 2, 20, 16, 128)
+            == esd.decode_multi_workspace_bytes(3, 8, 2, 2, 320, 128))
+    assert esd.decode_paged_workspace_bytes(3, 8, 2, 2, 1 << 20, 1 << 12, 128) == 0
+    assert _decp(B=0, q=None, k=None, v=None, table=None, lens=None, o=None, ws=None, wsb=0) == 0
+
+
 def test_decode_multi_empty_is_a_noop():
     assert _decm(B=0, q=None, k=None, v=None, lens=None, o=None, ws=None, wsb=0) == 0
 

@@ -1,0 +1,107 @@
+"""GPU parity of paged-cache decode (attn_decode_paged) against the oracle.
+
+Token p of sequence b lives in pool block table[b][p // block_size] at row
+p % block_size ("Attention mechanisms: from alignment to efficient long
+context", section 20).  The pools hold NaN in every row no sequence owns (spare
+blocks, the tail of each last block) and the tables hold -1 past each
+sequence's blocks, so a read of anything outside the sequence would show.
+Tolerances as for contiguous decode (bf16: max|dO| <= 1e-2, max|dlse| <= 1e-3);
+paged and contiguous decode of the same rows must agree bit for bit, since the
+arithmetic and its order are the same.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle.dense as oa
+import workloads as W
+from gpu_util import check, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+esd = pytest.importorskip("exact_scaled_dot_amd")
+
+LENS = np.array([0, 1, 2, 15, 16, 17, 31, 33, 127, 1023, 1024, 1025, 1040, 2100, 3000],
+                dtype=np.int32)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    esd.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _run(q, kp, vp, table, lens, scale, rope_base=0.0):
+    import torch
+    o, lse = esd.decode_paged(dev(q), dev(kp), dev(vp), dev(table), dev(lens), scale=scale,
+                              rope_base=rope_base)
+    torch.cuda.synchronize()
+    return host(o), host(lse)
+
+
+def _check_rows(o, lse, ro, rl, what):
+    dead = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(lse), dead), what
+    assert np.all(o[dead] == 0), what
+    live = ~dead
+    check(o[live], lse[live], ro[live], rl[live], "bf16", what)
+
+
+@pytest.mark.parametrize("bs", [16, 32, 64, 256])
+@pytest.mark.parametrize("Hq,Hkv,T", [(32, 8, 1), (32, 8, 4), (8, 8, 2), (16, 2, 1)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_paged_shapes(bs, Hq, Hkv, T, d):
+    w = W.WORKLOADS["c4"]
+    q, kp, vp, table = W.paged_inputs(w, LENS, block_size=bs, T=T, Hq=Hq, Hkv=Hkv, d=d,
+                                      seed_base=9800 + bs + Hq + T + d)
+    scale = 1 / math.sqrt(d)
+    o, lse = _run(q, kp, vp, table, LENS, scale)
+    ro, rl = oa.decode_paged(q, kp, vp, table, LENS, block_size=bs, scale=scale, dtype="bf16")
+    _check_rows(o, lse, ro, rl, f"paged bs={bs} Hq={Hq} Hkv={Hkv} T={T} d={d}")
+
+
+@pytest.mark.parametrize("bs", [16, 128])
+def test_decode_paged_equals_contiguous(bs):
+    """The same rows laid out contiguously give identical outputs."""
+    import torch
+    w = W.WORKLOADS["c4"]
+    q, kp, vp, table = W.paged_inputs(w, LENS, block_size=bs, T=3, Hq=32, Hkv=8, d=128,
+                                      seed_base=9900 + bs)
+    o, lse = _run(q, kp, vp, table, LENS, 0.0884, rope_base=10000.0)
+    max_len = int(LENS.max())
+    kc = np.full((len(LENS), 8, max_len, 128), W.BF16_NAN_BITS, dtype=np.uint16)
+    vc = kc.copy()
+    for b, n in enumerate(LENS):
+        pos = np.arange(n)
+        kc[b, :, :n] = kp[table[b, pos // bs], :, pos % bs].transpose(1, 0, 2)
+        vc[b, :, :n] = vp[table[b, pos // bs], :, pos % bs].transpose(1, 0, 2)
+    oc, lc = esd.decode_multi(dev(q), dev(kc), dev(vc), dev(LENS), scale=0.0884, rope_base=10000.0)
+    torch.cuda.synchronize()
+    assert np.array_equal(o, host(oc)) and np.array_equal(lse, host(lc))
+
+
+def test_decode_paged_rope():
+    w = W.WORKLOADS["c4"]
+    q, kp, vp, table = W.paged_inputs(w, LENS, block_size=16, T=2, Hq=16, Hkv=4, d=128,
+                                      seed_base=9950)
+    o, lse = _run(q, kp, vp, table, LENS, 0.0884, rope_base=10000.0)
+    ro, rl = oa.decode_paged(q, kp, vp, table, LENS, block_size=16, scale=0.0884,
+                             rope_base=10000.0, dtype="bf16")
+    _check_rows(o, lse, ro, rl, "paged rope")
+
+
+def test_decode_paged_c4_shape():
+    """The GQA decode batch (B=32, Hq=32, Hkv=8, d=128, lengths 1024..32768) in
+    16-token blocks scattered over the pool."""
+    w = W.WORKLOADS["c4"]
+    lens = W.decode_lens(w)
+    q, kp, vp, table = W.paged_inputs(w, lens, block_size=16)
+    say(f"c4 paged: {kp.shape[0]} blocks of 16, lens sum {lens.sum()}")
+    o, lse = _run(q, kp, vp, table, lens, w.scale)
+    ro, rl = oa.decode_paged(q, kp, vp, table, lens, block_size=16, scale=w.scale, dtype="bf16")
+    _check_rows(o, lse, ro, rl, "paged c4")

@@ -169,3 +169,48 @@ def decode_inputs(w: Workload, lens: np.ndarray, *, Hq=None, Hkv=None, max_len=N
         kc[b, :, :n] = f32_to_bf16_bits(kb)
         vc[b, :, :n] = f32_to_bf16_bits(vb)
     return q, kc, vc
+
+
+def paged_inputs(w: Workload, lens: np.ndarray, *, block_size: int = 16, T: int = 1, Hq=None,
+                 Hkv=None, d=None, seed_base=None, spare_blocks: int = 8, max_blocks=None):
+    """q [B,Hq,T,d], K/V pools [num_blocks,Hkv,block_size,d] (bf16 bits) and an
+    int32 block table [B, max_blocks] for a paged decode workload.
+
+    Sequence b owns ceil(len_b / block_size) physical blocks taken in order from
+    one seeded permutation of the pool (so logically adjacent blocks sit at
+    unrelated physical places); ``spare_blocks`` more blocks stay unowned.  Its
+    rows are drawn per sequence in order from one generator per tensor, with
+    the same distribution as ``decode_inputs``.  Every pool row that no sequence
+    owns (spare blocks and the tail of each last block) holds bf16 NaN, and
+    table entries past a sequence's blocks are -1.
+    """
+    B = len(lens)
+    Hq = w.Hq if Hq is None else Hq
+    Hkv = w.Hkv if Hkv is None else Hkv
+    d = w.d if d is None else d
+    s = w.seed_base if seed_base is None else seed_base
+    bs = block_size
+    nb = [(int(n) + bs - 1) // bs for n in lens]
+    mb = max(nb + [1]) if max_blocks is None else max_blocks
+    num_blocks = sum(nb) + spare_blocks
+    perm = np.random.default_rng(s + 5).permutation(num_blocks).astype(np.int32)
+    table = np.full((B, mb), -1, dtype=np.int32)
+    kp = np.full((num_blocks, Hkv, bs, d), BF16_NAN_BITS, dtype=np.uint16)
+    vp = np.full((num_blocks, Hkv, bs, d), BF16_NAN_BITS, dtype=np.uint16)
+    q = normal((B, Hq, T, d), s + 1, w.sigma_qk, "bf16")
+    rk = np.random.default_rng(s + 2)
+    rv = np.random.default_rng(s + 3)
+    off = 0
+    for b in range(B):
+        n = int(lens[b])
+        phys = perm[off:off + nb[b]]
+        off += nb[b]
+        table[b, :nb[b]] = phys
+        for pool, r, sig in ((kp, rk, w.sigma_qk), (vp, rv, w.sigma_v)):
+            x = r.standard_normal((Hkv, n, d), dtype=np.float32)
+            if sig != 1.0:
+                x *= np.float32(sig)
+            full = np.full((Hkv, nb[b] * bs, d), BF16_NAN_BITS, dtype=np.uint16)
+            full[:, :n] = f32_to_bf16_bits(x)
+            pool[phys] = full.reshape(Hkv, nb[b], bs, d).transpose(1, 0, 2, 3)
+    return q, kp, vp, table
