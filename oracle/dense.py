@@ -333,3 +333,72 @@ def decode_paged(q, k_pool, v_pool, block_table, seq_lens, *, block_size: int, s
         kc[b, :, :n] = gather_paged(k_pool, block_table, n, b, block_size)
         vc[b, :, :n] = gather_paged(v_pool, block_table, n, b, block_size)
     return decode_multi(q, kc, vc, seq_lens, scale=scale, rope_base=rope_base, dtype=dtype)
+
+
+def rope_transpose(g, positions, base: float):
+    """Adjoint of the RoPE rotation: the rotation by the negative angle, no rounding.
+
+    Carries a gradient taken with respect to rotated rows back to the rows
+    before rotation (each pair rotation is orthogonal, so its transpose is its
+    inverse).
+    """
+    g = np.asarray(g, np.float64)
+    d = g.shape[-1]
+    positions = np.asarray(positions, dtype=np.int64)
+    cos_t, sin_t = rope_cos_sin(int(positions.max()) + 1, d, base)
+    c, s = cos_t[positions], sin_t[positions]
+    g0, g1 = g[..., 0::2], g[..., 1::2]
+    out = np.empty_like(g)
+    out[..., 0::2] = g0 * c + g1 * s
+    out[..., 1::2] = -g0 * s + g1 * c
+    return out
+
+
+def attention_bwd(q, k, v, do, *, causal: bool, scale: float, rope_base: float = 0.0,
+                  dtype: str = "bf16", window: int = 0):
+    """Gradients dQ, dK, dV (fp64) of L = sum(dO * O) for O = attention(q, k, v).
+
+    The pages state only that the backward pass recomputes the score tiles
+    from the saved per-row statistics ("Transformer Architecture
+    Deconstructed", recomputation strategy; "Attention mechanisms: from
+    alignment to efficient long context", section 19); the gradient itself is
+    that of the function ``attention`` defines, written out per head:
+      P = softmax(S), S = scale * Q K^T + M     (masked entries have P = 0)
+      dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(P * dP)),
+      dQ = scale * dS K,  dK = scale * dS^T Q.
+    Query heads that share a KV head add their dK and dV.  With RoPE, Q and K
+    enter as rotated and rounded rows; the rounding is taken as the identity
+    and the rotation's transpose carries dQ and dK back to the unrotated rows.
+    q [B,Hq,Nq,d], k, v [B,Hkv,Nk,d], do [B,Hq,Nq,d] (any real dtype, or uint16
+    bf16 bits); returns dq [B,Hq,Nq,d], dk, dv [B,Hkv,Nk,d].
+    """
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    if (causal or window or rope_base) and Nq > Nk:
+        raise ValueError("causal, windowed or rotated attention needs Nq <= Nk")
+    q_pos = np.arange(Nq) + (Nk - Nq)
+    k_pos = np.arange(Nk)
+    dq = np.zeros((B, Hq, Nq, d))
+    dk = np.zeros((B, Hkv, Nk, d))
+    dv = np.zeros((B, Hkv, Nk, d))
+    for b in range(B):
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            qh, kh, vh = _f64(q[b, h]), _f64(k[b, g]), _f64(v[b, g])
+            doh = _f64(do[b, h])
+            if rope_base:
+                qh = rope(qh, q_pos, rope_base, dtype)
+                kh = rope(kh, k_pos, rope_base, dtype)
+            _, p = scores_and_weights(qh, kh, scale=scale, causal=causal, q_pos=q_pos,
+                                      k_pos=k_pos, window=window)
+            dv[b, g] += p.T @ doh
+            dp = doh @ vh.T
+            ds = p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
+            dqh = scale * (ds @ kh)
+            dkh = scale * (ds.T @ qh)
+            if rope_base:
+                dqh = rope_transpose(dqh, q_pos, rope_base)
+                dkh = rope_transpose(dkh, k_pos, rope_base)
+            dq[b, h] = dqh
+            dk[b, g] += dkh
+    return dq, dk, dv

@@ -518,4 +518,73 @@ def pin_paged_decode_equals_contiguous():
         assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]), bs
 
 
+def _torch_rope(x, positions, base):
+    """RoPE in torch fp64 as complex multiplication ([Breakdown] Key Topic 4),
+    differentiable, unrounded."""
+    import torch
+    d = x.shape[-1]
+    th = torch.tensor([base ** (-2.0 * t / d) for t in range(d // 2)], dtype=torch.float64)
+    ang = torch.tensor(positions, dtype=torch.float64)[:, None] * th[None, :]
+    z = torch.view_as_complex(x.reshape(*x.shape[:-1], d // 2, 2).contiguous())
+    return torch.view_as_real(z * torch.polar(torch.ones_like(ang), ang)).reshape(x.shape)
+
+
+def pin_backward_against_autograd():
+    """dQ, dK, dV equal torch's fp64 autograd through scaled_dot_product_attention
+    (GQA by enable_gqa, causal by an explicit bottom-right mask, RoPE by a
+    differentiable complex rotation; inputs already representable, so the
+    oracle's rounding of rotated rows only matters with RoPE, where autograd
+    sees unrounded rows: compared there with f64 rounding)."""
+    import torch
+    import torch.nn.functional as F
+    cases = [(1, 2, 2, 5, 5, 8, False, 0.0, 0), (2, 4, 2, 6, 9, 8, True, 0.0, 0),
+             (1, 4, 1, 7, 7, 4, True, 100.0, 0), (1, 2, 1, 8, 8, 8, True, 0.0, 3)]
+    for n, (B, Hq, Hkv, Nq, Nk, d, causal, base, win) in enumerate(cases):
+        q, k, v = _rand_inputs(400 + n, B, Hq, Hkv, Nq, Nk, d, "f64")
+        do = _rng(410 + n).standard_normal((B, Hq, Nq, d))
+        dq, dk, dv = oa.attention_bwd(q, k, v, do, causal=causal, scale=0.35, rope_base=base,
+                                      dtype="f64", window=win)
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        qq, kk = tq, tk
+        if base:
+            qq = _torch_rope(tq, np.arange(Nq) + Nk - Nq, base)
+            kk = _torch_rope(tk, np.arange(Nk), base)
+        mask = None
+        if causal:
+            i = np.arange(Nq)[:, None] + (Nk - Nq)
+            j = np.arange(Nk)[None, :]
+            m = j <= i
+            if win:
+                m &= i - j < win
+            mask = torch.tensor(m)
+        o = F.scaled_dot_product_attention(qq, kk, tv, attn_mask=mask, scale=0.35, enable_gqa=True)
+        o.backward(torch.tensor(do))
+        for got, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+            assert np.max(np.abs(got - ref.numpy())) < 1e-12, n
+
+
+def pin_backward_finite_differences():
+    """Central differences of L = sum(dO * O) in fp64 agree with the gradients
+    (no library involved: the loss is the oracle's own forward)."""
+    B, Hq, Hkv, Nq, Nk, d = 1, 2, 1, 4, 6, 4
+    q, k, v = _rand_inputs(430, B, Hq, Hkv, Nq, Nk, d, "f64")
+    do = _rng(431).standard_normal((B, Hq, Nq, d))
+
+    def loss(q_, k_, v_):
+        o, _ = oa.attention(q_, k_, v_, causal=True, scale=0.5, dtype="f64")
+        return float(np.sum(o * do))
+
+    dq, dk, dv = oa.attention_bwd(q, k, v, do, causal=True, scale=0.5, dtype="f64")
+    eps = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        for idx in [(0, 0, 0, 0), (0, 0, 2, 3), (0, x.shape[1] - 1, x.shape[2] - 1, 1)]:
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = [xp if y is x else y for y in (q, k, v)]
+            args_m = [xm if y is x else y for y in (q, k, v)]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(fd - g[idx]) < 1e-7 * max(1.0, abs(fd)), (idx, fd, g[idx])
+
+
 ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

@@ -133,7 +133,40 @@ def _gather_swapped(pool, block_table, n, b, block_size):
     return np.transpose(np.asarray(rows, np.float64), (1, 0, 2))
 
 
+def _rope_transpose_forward(g, positions, base):
+    # rotates forward instead of by the negative angle
+    return _rope_generic(g, positions, base, "f64")
+
+
+def _bwd_without_rowsum(q, k, v, do, *, causal, scale, rope_base=0.0, dtype="bf16", window=0):
+    # dS = P * dP, the softmax Jacobian's rowsum term dropped
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    dq = np.zeros((B, Hq, Nq, d))
+    dk = np.zeros((B, Hkv, Nk, d))
+    dv = np.zeros((B, Hkv, Nk, d))
+    qp, kp = np.arange(Nq) + Nk - Nq, np.arange(Nk)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            qh, kh, vh = (np.asarray(x, np.float64) for x in (q[b, h], k[b, g], v[b, g]))
+            if rope_base:
+                qh, kh = oa.rope(qh, qp, rope_base, dtype), oa.rope(kh, kp, rope_base, dtype)
+            _, p = oa.scores_and_weights(qh, kh, scale=scale, causal=causal, q_pos=qp, k_pos=kp,
+                                         window=window)
+            dv[b, g] += p.T @ do[b, h]
+            ds = p * (do[b, h] @ vh.T)
+            dqh, dkh = scale * ds @ kh, scale * ds.T @ qh
+            if rope_base:
+                dqh, dkh = oa.rope_transpose(dqh, qp, rope_base), oa.rope_transpose(dkh, kp, rope_base)
+            dq[b, h] = dqh
+            dk[b, g] += dkh
+    return dq, dk, dv
+
+
 MUTATIONS = {
+    "bwd_rope_not_transposed": ("rope_transpose", _rope_transpose_forward),
+    "bwd_dropped_rowsum": ("attention_bwd", _bwd_without_rowsum),
     "paged_index_swapped": ("gather_paged", _gather_swapped),
     "decode_multi_hides_self": ("decode_multi", _decode_multi_hides_self),
     "window_off_by_one": ("scores_and_weights", _scores_window_le),
