@@ -250,6 +250,42 @@ def extra_decode_paged(torch, esd, stream, w, lens, reps=10):
             "ms": float(np.mean(ms)), "gbs": nb / (float(np.mean(ms)) * 1e-3) / 1e9}
 
 
+def extra_backward(torch, esd, stream, w, reps=5):
+    """TFLOP/s of the backward pass (attn_bwd after attn_fwd) on a prefill
+    workload.  Flops: the five products of the gradient (S, dP, dV, dQ, dK)
+    over the visible pairs, 2.5x the forward's two; the recomputation of S and
+    dP in the dQ kernel is not counted."""
+    print(f"[bench] extra workload backward {w.name}", file=sys.stderr, flush=True)
+    q, k, v = W.fwd_inputs(w)
+    dq_, dk_, dv_ = dev(q), dev(k), dev(v)
+    del q, k, v
+    do = dev(W.normal((w.B, w.Hq, w.Nq, w.d), 11500, 1.0, "f32"))
+    o, lse = esd.fwd(dq_, dk_, dv_, causal=w.causal, scale=w.scale, rope_base=w.rope_base)
+    gq = torch.empty((w.B, w.Hq, w.Nq, w.d), dtype=torch.float32, device="cuda")
+    gk = torch.empty((w.B, w.Hkv, w.Nk, w.d), dtype=torch.float32, device="cuda")
+    gv = torch.empty_like(gk)
+    ws = torch.empty(esd.bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.rope_base,
+                                             esd.ATTN_BF16), dtype=torch.uint8, device="cuda")
+    call = lambda: esd.bwd(dq_, dk_, dv_, o, lse, do, causal=w.causal, scale=w.scale,
+                           rope_base=w.rope_base, dq=gq, dk=gk, dv=gv, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    fl = 2.5 * fwd_flops(w)
+    del dq_, dk_, dv_, do, o, lse, gq, gk, gv, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"{w.note}, backward (dQ, dK, dV)", "flops": fl, "ms": float(np.mean(ms)),
+            "tflops": fl / (float(np.mean(ms)) * 1e-3) / 1e12}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -409,6 +445,7 @@ def main():
         del dq, dk, dv, o3, l3, ws3, kr3, dqd, o4, l4, ws4
         torch.cuda.empty_cache()
         rec["extra"] = extra_prefill(torch, esd, stream)
+        rec["extra"]["c3_backward"] = extra_backward(torch, esd, stream, w3)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(w3, w4)

@@ -9,6 +9,7 @@ fallback: if the library is missing, every call raises.
 Functions (same names as the C entry points):
   fwd(q, k, v, causal, scale=None, rope_base=0.0, out=None, lse=None, workspace=None,
       window=0)       (window > 0: attn_fwd_window, causal sliding window)
+  bwd(q, k, v, o, lse, dout, causal, scale=None, rope_base=0.0, workspace=None)
   decode(q, k_cache, v_cache, seq_lens, scale=None, out=None, lse=None, workspace=None)
   decode_multi(q, k_cache, v_cache, seq_lens, scale=None, rope_base=0.0, out=None, lse=None,
                workspace=None)   (q [B,Hq,T,d]: T new tokens per sequence)
@@ -34,6 +35,7 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID", 2: "ATTN_ERR_UNSUPPORTED", 3: "AT
           4: "ATTN_ERR_WORKSPACE"}
 
 EXPORTS = ("attn_status_str", "attn_fwd_workspace_bytes", "attn_fwd", "attn_fwd_window",
+           "attn_bwd_workspace_bytes", "attn_bwd",
            "attn_decode_workspace_bytes", "attn_decode", "attn_decode_multi_workspace_bytes",
            "attn_decode_multi", "attn_decode_paged_workspace_bytes", "attn_decode_paged",
            "attn_rope_apply")
@@ -65,6 +67,11 @@ def lib():
     L.attn_fwd.restype = i
     L.attn_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, f, i, vp, sz, vp]
     L.attn_fwd_window.restype = i
+    L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, f, i]
+    L.attn_bwd_workspace_bytes.restype = sz
+    L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, f, i, vp,
+                           sz, vp]
+    L.attn_bwd.restype = i
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
@@ -168,6 +175,46 @@ def fwd(q, k, v, causal: bool, scale=None, rope_base: float = 0.0, out=None, lse
                                   Nq, Nk, d, int(bool(causal)), float(scale), float(rope_base),
                                   code, _ptr(workspace), wsb, _stream()))
     return out, lse
+
+
+def bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, rope_base, dtype_code) -> int:
+    return int(lib().attn_bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, float(rope_base), dtype_code))
+
+
+def bwd(q, k, v, o, lse, dout, causal: bool, scale=None, rope_base: float = 0.0, dq=None,
+        dk=None, dv=None, workspace=None):
+    """dq [B,Hq,Nq,d], dk, dv [B,Hkv,Nk,d] (fp32) of sum(dout * O) for O = fwd(q, k, v)."""
+    import torch
+    L = lib()
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("dout", dout)):
+        _need_cuda_contig(n, t)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    if o.dtype != torch.float32 or lse.dtype != torch.float32 or dout.dtype != torch.float32:
+        raise TypeError("o, lse and dout must be float32")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk_ = k.shape
+    if ((Bk, dk_) != (B, d) or tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape)
+            or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, Nq)):
+        raise ValueError("shape mismatch between q, k, v, o, lse and dout")
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if dq is None:
+        dq = torch.empty((B, Hq, Nq, d), dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty((B, Hkv, Nk, d), dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty((B, Hkv, Nk, d), dtype=torch.float32, device=q.device)
+    need = bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, rope_base, code)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("attn_bwd", L.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                  _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, Nq, Nk, d,
+                                  int(bool(causal)), float(scale), float(rope_base), code,
+                                  _ptr(workspace), wsb, _stream()))
+    return dq, dk, dv
 
 
 def decode(q, k_cache, v_cache, seq_lens, scale=None, out=None, lse=None, workspace=None,

@@ -20,12 +20,17 @@ OUT = os.path.join(HERE, "libattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["attn_host.cpp", "rope.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip"]
+SOURCES = ["attn_host.cpp", "rope.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip",
+           "backward.hip"]
 
 # Per-source extra flags.  The bf16 kernels never see NaN (inputs are finite by
 # contract; masking uses -inf), so max chains need no NaN canonicalisation and
 # fold into v_max3_f32.
-EXTRA = {"prefill_bf16.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"]}
+EXTRA = {"prefill_bf16.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"],
+         # matrix-core results in vector registers: the score tiles feed the
+         # vector ALU every tile, and copying them out of accumulation
+         # registers cost more instructions than the products themselves
+         "backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -269,6 +269,98 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                              scale, 0.f, dtype, workspace, workspace_bytes, stream);
 }
 
+// Workspace of attn_bwd, in order (each section 256-byte aligned): dO in bf16
+// [B,Hq,Nq,d], D [B,Hq,Nq] fp32, lse2 [B,Hq,Nq] fp32, then with RoPE the
+// rotated Q [B,Hq,Nq,d] and K [B,Hkv,Nk,d] in bf16.
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, float rope_base,
+                                attn_dtype dtype) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0 || dtype != ATTN_BF16)
+        return 0;
+    const size_t rows = (size_t)B * Hq * Nq;
+    size_t n = align256(rows * d * 2) + 2 * align256(rows * 4);
+    if (rope_base > 0.f) n += align256(rows * d * 2) + align256((size_t)B * Hkv * Nk * d * 2);
+    return n;
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
+             const float* dout, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int Nq,
+             int Nk, int d, int causal, float scale, float rope_base, attn_dtype dtype,
+             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (B < 0 || Hq < 0 || Nq < 0) return fail(ATTN_ERR_INVALID, "negative size");
+    if (Hkv < 1 || Nk < 1 || d < 1) return fail(ATTN_ERR_INVALID, "Hkv, Nk and d must be >= 1");
+    if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID, "Hq must be a multiple of Hkv");
+    if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID, "causal must be 0 or 1");
+    if (causal && Nq > Nk) return fail(ATTN_ERR_INVALID, "causal needs Nq <= Nk");
+    if (!(std::isfinite(scale) && scale > 0.f)) return fail(ATTN_ERR_INVALID, "scale must be finite and > 0");
+    if (rope_base != 0.f && !(std::isfinite(rope_base) && rope_base > 0.f))
+        return fail(ATTN_ERR_INVALID, "rope_base must be 0 or a finite positive base");
+    if (rope_base != 0.f && Nq > Nk)
+        return fail(ATTN_ERR_INVALID, "RoPE needs Nq <= Nk (query positions Nk-Nq+i must be >= 0)");
+    if (!known_dtype(dtype)) return fail(ATTN_ERR_INVALID, "unknown dtype");
+    if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "the backward pass is built for bf16");
+    if (!supported_d(d)) return fail(ATTN_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+    if ((long long)Nk * d * 4 >= (1LL << 31) || (long long)Nq * d * 4 >= (1LL << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "one head's Q, K or V must be under 2 GiB (32-bit buffer offsets)");
+    if (B == 0 || Hq == 0 || Nq == 0) return ATTN_OK;
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+        return fail(ATTN_ERR_INVALID, "null pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+        !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+        return fail(ATTN_ERR_INVALID, "q, k, v, o, dout, dq, dk, dv must be 16-byte aligned");
+    const size_t need = attn_bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, rope_base, dtype);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "backward workspace missing or too small");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(ATTN_ERR_INVALID, "backward workspace must be 256-byte aligned");
+
+    const size_t rows = (size_t)B * Hq * Nq;
+    char* w = static_cast<char*>(workspace);
+    attn::BwdArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.o = o; a.lse = lse; a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.d = d;
+    a.causal = causal; a.scale = scale;
+    a.do16 = reinterpret_cast<uint16_t*>(w);
+    w += align256(rows * d * 2);
+    a.dvec = reinterpret_cast<float*>(w);
+    w += align256(rows * 4);
+    a.lse2 = reinterpret_cast<float*>(w);
+    w += align256(rows * 4);
+    const double2* tab = nullptr;
+    hipError_t e = hipSuccess;
+    if (rope_base > 0.f) {
+        int dev = 0;
+        e = hipGetDevice(&dev);
+        if (e != hipSuccess) return fail(ATTN_ERR_HIP, "hipGetDevice");
+        tab = attn::rope_table(dev, rope_base, d, Nk, &e);
+        if (!tab) return fail(ATTN_ERR_HIP, "RoPE table");
+        uint16_t* qr = reinterpret_cast<uint16_t*>(w);
+        w += align256(rows * d * 2);
+        uint16_t* kr = reinterpret_cast<uint16_t*>(w);
+        // the rotated operands exactly as the forward pass forms them
+        e = attn::launch_rope_bf16(a.q, qr, (long long)rows, Nq, d, Nk - Nq, tab, stream);
+        if (e == hipSuccess)
+            e = attn::launch_rope_bf16(a.k, kr, (long long)B * Hkv * Nk, Nk, d, 0, tab, stream);
+        if (e != hipSuccess) return fail(ATTN_ERR_HIP, "rope launch");
+        a.q = qr;
+        a.k = kr;
+    }
+    e = attn::launch_bwd_bf16(a, stream);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, hipGetErrorString(e));
+    if (rope_base > 0.f) {
+        // gradients with respect to the rotated rows -> the rows before rotation
+        e = attn::launch_rope_f32_transpose(dq, dq, (long long)rows, Nq, d, Nk - Nq, tab, stream);
+        if (e == hipSuccess)
+            e = attn::launch_rope_f32_transpose(dk, dk, (long long)B * Hkv * Nk, Nk, d, 0, tab, stream);
+        if (e != hipSuccess) return fail(ATTN_ERR_HIP, hipGetErrorString(e));
+    }
+    return ATTN_OK;
+}
+
 int attn_rope_apply(const void* x, void* out, int B, int H, int N, int d,
                     int pos_offset, float rope_base, attn_dtype dtype,
                     hipStream_t stream) {

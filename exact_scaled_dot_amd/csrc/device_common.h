@@ -61,6 +61,19 @@ __device__ __forceinline__ uint4 rope8_bf16(uint4 x, const double2* __restrict__
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// One pair rotated by the negative angle (the transpose of rope_pair_f64).
+__device__ __forceinline__ void rope_pair_t_f64(float x0, float x1, double c, double s,
+                                                float& r0, float& r1) {
+#pragma clang fp contract(off)
+    double a = (double)x0, b = (double)x1;
+    double p0 = a * c;
+    double p1 = b * s;
+    double p2 = a * s;
+    double p3 = b * c;
+    r0 = (float)(p0 + p1);
+    r1 = (float)(p3 - p2);
+}
+
 // Rotate 4 consecutive fp32 elements (2 pairs).
 __device__ __forceinline__ float4 rope4_f32(float4 x, const double2* __restrict__ tab_row, int d0) {
     const double2* t = tab_row + (d0 >> 1);

@@ -53,6 +53,31 @@ constexpr int kDecodeChunk = 1024;  // keys per split workgroup
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
+struct BwdArgs {
+    const uint16_t* q;   // rotated Q when RoPE is on
+    const uint16_t* k;   // rotated K when RoPE is on
+    const uint16_t* v;
+    const float* o;
+    const float* lse;
+    const float* dout;
+    float* dq;
+    float* dk;
+    float* dv;
+    int B, Hq, Hkv, Nq, Nk, d;
+    int causal;
+    float scale;
+    uint16_t* do16;  // workspace: dO in bf16 [B, Hq, Nq, d]
+    float* dvec;     // workspace: rowsum(dO * O) [B, Hq, Nq]
+    float* lse2;     // workspace: lse * log2(e) [B, Hq, Nq]
+};
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+
+// out[bh, n, :] = rotate(x[bh, n, :], -(pos_offset + n)) in fp64, rounded to fp32:
+// the transpose of the RoPE rotation, for gradients.
+hipError_t launch_rope_f32_transpose(const float* x, float* out, long long rows, int N, int d,
+                                     int pos_offset, const double2* tab, hipStream_t stream);
+
 // Device table of (cos, sin) in fp64, [npos][d/2]; created or grown on demand.
 // Returns null on failure (HIP error stored in *err).
 const double2* rope_table(int device, float base, int d, int npos, hipError_t* err);

@@ -113,6 +113,40 @@ int attn_fwd_window(const void* q, const void* k, const void* v, float* o, float
                     float scale, float rope_base, attn_dtype dtype,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of workspace attn_bwd needs: dO in bf16 and two fp32 values per query
+ * row, plus the rotated Q and K (bf16) when rope_base > 0; 0 for fp32. */
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, float rope_base,
+                                attn_dtype dtype);
+
+/*
+ * Backward pass of attn_fwd: the gradients of L = sum(dout * O) with respect
+ * to q, k and v.  The score tiles are recomputed from q, k and the forward's
+ * lse instead of being stored ("Transformer Architecture Deconstructed",
+ * recomputation strategy in the backward pass; "Attention mechanisms: from
+ * alignment to efficient long context", section 19).  With P the attention
+ * weights (masked entries 0):
+ *   dV = P^T dO,  dS = P * (dO V^T - rowsum(dO * O)),
+ *   dQ = scale * dS K,  dK = scale * dS^T Q,
+ * summed over the query heads that share a KV head.  With RoPE the gradients
+ * are taken with respect to the rows before rotation (the rounding of the
+ * rotated rows counts as the identity).
+ *   q, k, v    device bf16, as given to attn_fwd (dtype must be ATTN_BF16).
+ *   o, lse     device fp32 [B,Hq,Nq,d], [B,Hq,Nq]: attn_fwd's outputs for the
+ *              same arguments.
+ *   dout       device fp32 [B,Hq,Nq,d] upstream gradient; rounded to bf16 for
+ *              the matrix products.
+ *   dq         device fp32 [B,Hq,Nq,d];  dk, dv  device fp32 [B,Hkv,Nk,d]
+ *              (written, not accumulated).
+ *   causal, scale, rope_base  as attn_fwd.
+ *   workspace  device buffer of attn_bwd_workspace_bytes(...) bytes, 256-byte
+ *              aligned.
+ * Errors as attn_fwd; ATTN_F32 returns ATTN_ERR_UNSUPPORTED.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
+             const float* dout, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int Nq,
+             int Nk, int d, int causal, float scale, float rope_base, attn_dtype dtype,
+             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace attn_decode needs for partial (max/sum, O) states. */
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int d);
 

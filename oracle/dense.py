@@ -402,3 +402,56 @@ def attention_bwd(q, k, v, do, *, causal: bool, scale: float, rope_base: float =
             dq[b, h] = dqh
             dk[b, g] += dkh
     return dq, dk, dv
+
+
+def attention_bwd_rows(q, k, v, do, b: int, g: int, q_rows, k_rows, *, causal: bool,
+                       scale: float, rope_base: float = 0.0, dtype: str = "bf16"):
+    """Selected rows of the backward pass for KV head g of batch b.
+
+    Same gradient as ``attention_bwd``, evaluated only where asked: dQ for the
+    query rows ``q_rows`` of every query head that reads KV head g, and dK, dV
+    for the key rows ``k_rows`` of KV head g.  rowsum(P * dP) is taken as
+    dO . O, the identity that follows from O = P V, with O and lse from
+    ``attention_rows`` over every query row of those heads.  Returns
+    dq [G, len(q_rows), d], dk [len(k_rows), d], dv [len(k_rows), d].
+    """
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    G = Hq // Hkv
+    q_rows = np.asarray(q_rows, dtype=np.int64)
+    k_rows = np.asarray(k_rows, dtype=np.int64)
+    q_pos = np.arange(Nq) + (Nk - Nq)
+    k_pos = np.arange(Nk)
+    kg, vg = _f64(k[b, g]), _f64(v[b, g])
+    if rope_base:
+        kg = rope(kg, k_pos, rope_base, dtype)
+    dq = np.zeros((G, len(q_rows), d))
+    dk = np.zeros((len(k_rows), d))
+    dv = np.zeros((len(k_rows), d))
+    kc: dict = {}
+    for hh in range(G):
+        h = g * G + hh
+        o, lse = attention_rows(q, k, v, b, h, np.arange(Nq), causal=causal, scale=scale,
+                                rope_base=rope_base, dtype=dtype, _kcache=kc)
+        doh = _f64(do[b, h])
+        dvec = np.sum(doh * o, axis=-1)
+        qh = _f64(q[b, h])
+        if rope_base:
+            qh = rope(qh, q_pos, rope_base, dtype)
+        # dQ rows: P row, dP row, dS row
+        s_r, _ = scores_and_weights(qh[q_rows], kg, scale=scale, causal=causal,
+                                    q_pos=q_pos[q_rows], k_pos=k_pos)
+        p_r = np.exp(s_r - lse[q_rows][:, None])
+        ds_r = p_r * (doh[q_rows] @ vg.T - dvec[q_rows][:, None])
+        dq_h = scale * (ds_r @ kg)
+        dq[hh] = rope_transpose(dq_h, q_pos[q_rows], rope_base) if rope_base else dq_h
+        # dK, dV rows: the score columns of the selected keys over every query
+        s_c, _ = scores_and_weights(qh, kg[k_rows], scale=scale, causal=causal,
+                                    q_pos=q_pos, k_pos=k_pos[k_rows])
+        p_c = np.exp(s_c - lse[:, None])
+        dv += p_c.T @ doh
+        ds_c = p_c * (doh @ vg[k_rows].T - dvec[:, None])
+        dk += scale * (ds_c.T @ qh)
+    if rope_base:
+        dk = rope_transpose(dk, k_pos[k_rows], rope_base)
+    return dq, dk, dv

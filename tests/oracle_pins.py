@@ -587,4 +587,21 @@ def pin_backward_finite_differences():
             assert abs(fd - g[idx]) < 1e-7 * max(1.0, abs(fd)), (idx, fd, g[idx])
 
 
+def pin_backward_rows_equal_full():
+    """The row-sampled backward (rowsum(P * dP) taken as dO . O) equals the full
+    one on every sampled row, with and without RoPE."""
+    B, Hq, Hkv, Nq, Nk, d = 2, 4, 2, 9, 12, 8
+    for base, causal in ((0.0, True), (100.0, True), (0.0, False)):
+        q, k, v = _rand_inputs(440, B, Hq, Hkv, Nq, Nk, d, "bf16")
+        do = _rng(441).standard_normal((B, Hq, Nq, d))
+        dq, dk, dv = oa.attention_bwd(q, k, v, do, causal=causal, scale=0.3, rope_base=base,
+                                      dtype="bf16")
+        qr, kr = [0, 4, 8], [0, 3, 11]
+        sq, sk, sv = oa.attention_bwd_rows(q, k, v, do, 1, 1, qr, kr, causal=causal, scale=0.3,
+                                           rope_base=base, dtype="bf16")
+        assert np.max(np.abs(sq - dq[1, 2:4][:, qr])) < 1e-12
+        assert np.max(np.abs(sk - dk[1, 1, kr])) < 1e-12
+        assert np.max(np.abs(sv - dv[1, 1, kr])) < 1e-12
+
+
 ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

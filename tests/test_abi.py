@@ -174,6 +174,37 @@ def test_decode_paged_workspace_and_noop():
     assert _decp(B=0, q=None, k=None, v=None, table=None, lens=None, o=None, ws=None, wsb=0) == 0
 
 
+def _bwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, Hq=4, Hkv=2, Nq=8, Nk=8,
+             d=128, causal=1, scale=0.1, rope=0.0, dtype=esd.ATTN_BF16, ws=P, wsb=1 << 20)
+    a.update(kw)
+    return esd.lib().attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                              a["dv"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                              a["causal"], a["scale"], a["rope"], a["dtype"], a["ws"], a["wsb"],
+                              None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dq=None), 1), (dict(lse=None), 1), (dict(do=None), 1), (dict(Nq=9, Nk=8), 1),
+    (dict(causal=0, Nq=9, Nk=8, rope=100.0), 1), (dict(causal=3), 1), (dict(scale=-1.0), 1),
+    (dict(dtype=esd.ATTN_F32), 2), (dict(d=96), 2), (dict(ws=None), 4), (dict(wsb=64), 4),
+    (dict(ws=ctypes.c_void_p(272)), 1), (dict(dk=ctypes.c_void_p(260)), 1),
+])
+def test_bwd_rejects_on_host(kw, code):
+    assert _bwd(**kw) == code
+
+
+def test_bwd_workspace():
+    rows = 2 * 8 * 100
+    base = esd.bwd_workspace_bytes(2, 8, 2, 100, 300, 128, 0.0, esd.ATTN_BF16)
+    assert rows * 128 * 2 + 2 * rows * 4 <= base < rows * 128 * 2 + 2 * rows * 4 + 3 * 256
+    rope = esd.bwd_workspace_bytes(2, 8, 2, 100, 300, 128, 1e4, esd.ATTN_BF16)
+    assert rope - base >= rows * 128 * 2 + 2 * 2 * 300 * 128 * 2
+    assert esd.bwd_workspace_bytes(2, 8, 2, 100, 300, 128, 0.0, esd.ATTN_F32) == 0
+    assert _bwd(B=0, q=None, k=None, v=None, o=None, lse=None, do=None, dq=None, dk=None,
+                dv=None, ws=None, wsb=0) == 0
+
+
 def test_decode_multi_empty_is_a_noop():
     assert _decm(B=0, q=None, k=None, v=None, lens=None, o=None, ws=None, wsb=0) == 0
 
