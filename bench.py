@@ -392,8 +392,8 @@ def main():
     # the time of the step is the wall time; the K rotation timed separately is
     # not part of it
     wall -= float(np.sum(rope_ms)) * 1e-3 if do_pf else 0.0
-    pf_traffic = recorded_traffic("prefill_bf16_kernel<128, true, true>")
-    dec_split = recorded_traffic("decode_split_kernel<128, 4>")
+    pf_traffic = recorded_traffic("prefill_bf16_kernel<128, true, true, false>")
+    dec_split = recorded_traffic("decode_split_kernel<128, 4, false>")
     dec_merge = recorded_traffic("decode_merge_kernel<128>")
     dec_traffic = dec_split + dec_merge if dec_split is not None and dec_merge is not None else None
 
@@ -418,14 +418,14 @@ def main():
             "decode_bytes": nbytes, "decode_ms": dec_avg, "decode_ms_min": float(np.min(dec_ms)),
         },
         "roofline": {
-            "kernel": "prefill_bf16_kernel<128, true, true>",
+            "kernel": "prefill_bf16_kernel<128, true, true, false>",
             "bound": "mfma", "achieved": kern_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": (kern_tflops / PEAK_BF16_TFLOPS) if kern_tflops else None,
             "traffic": pf_traffic,
         },
         "decode": {
             "value": gbs, "unit": "GB/s",
-            "roofline": {"kernel": "decode_split_kernel<128, 4> + decode_merge_kernel<128>",
+            "roofline": {"kernel": "decode_split_kernel<128, 4, false> + decode_merge_kernel<128>",
                          "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": (gbs / PEAK_HBM_GBS) if gbs else None, "traffic": dec_traffic},
         },
