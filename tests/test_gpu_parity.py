@@ -222,3 +222,17 @@ def test_fwd_errors_raise():
     q = torch.zeros((1, 2, 8, 96), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(esd.AttnError):
         esd.fwd(q, q, q, causal=True)
+
+
+def test_decode_more_chunks_than_merge_slots():
+    """A 1.2M-key sequence: 1172 partial states of 1024 keys, more than the 1024
+    weights the merge kernel keeps in LDS, so the rest are recomputed."""
+    import torch
+    w = W.WORKLOADS["c4"]
+    lens = np.array([1_200_000, 5], dtype=np.int32)
+    q, kc, vc = W.decode_inputs(w, lens, Hq=4, Hkv=1, max_len=1_200_000, d=64, seed_base=7900)
+    say("decode: one sequence of 1.2M keys (1172 chunks)")
+    o, lse = esd.decode(dev(q), dev(kc), dev(vc), dev(lens), scale=0.125)
+    torch.cuda.synchronize()
+    ro, rl = oa.decode(q, kc, vc, lens, scale=0.125)
+    check(host(o), host(lse), ro, rl, "bf16", "decode 1.2M keys")
