@@ -116,10 +116,18 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     static_assert(NCH % NT == 0 || NT % NCH == 0, "tile/thread mismatch");
     constexpr int RS = D + kRP;  // stride of the row-read copies
     constexpr int TS = D + kTP;  // stride of the transposed-read copies
-    __shared__ __attribute__((aligned(16))) uint16_t Qr[2][kQT * RS];
-    __shared__ __attribute__((aligned(16))) uint16_t Or[2][kQT * RS];
-    __shared__ __attribute__((aligned(16))) uint16_t Qt[2][kQT * TS];
-    __shared__ __attribute__((aligned(16))) uint16_t Ot[2][kQT * TS];
+    // Tiles go from memory straight into LDS (buffer_load ... lds, 1 KB per
+    // instruction), so each copy is a separate object sized to whole
+    // instructions: the compiler then knows the loads into one buffer do not
+    // alias the reads from the other.
+    constexpr int RSZ = (kQT * RS + 511) / 512 * 512;
+    constexpr int TSZ = (kQT * TS + 511) / 512 * 512;
+    __shared__ __attribute__((aligned(16))) uint16_t Qr0[RSZ], Qr1[RSZ], Or0[RSZ], Or1[RSZ];
+    __shared__ __attribute__((aligned(16))) uint16_t Qt0[TSZ], Qt1[TSZ], Ot0[TSZ], Ot1[TSZ];
+    auto Qr = [&](int P) -> uint16_t* { return P ? Qr1 : Qr0; };
+    auto Or = [&](int P) -> uint16_t* { return P ? Or1 : Or0; };
+    auto Qt = [&](int P) -> uint16_t* { return P ? Qt1 : Qt0; };
+    auto Ot = [&](int P) -> uint16_t* { return P ? Ot1 : Ot0; };
     __shared__ __attribute__((aligned(16))) float Ls[2][kQT];
     __shared__ __attribute__((aligned(16))) float Dsh[2][kQT];
 
@@ -171,11 +179,29 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     // the first query row that sees this key (past the end of K: none)
     const int qmin = key < Nk ? (CAUSAL ? key - off : 0) : 0x7fffffff;
     struct Pair {
-        u32x4 q[LPT], o[LPT];
-        float l, d;
+        float l, d;  // this thread's slot of the tile's statistics
+    };
+    // One copy of a 32-row tile into LDS: instruction j writes 16-byte slots
+    // 64 j .. 64 j + 63, slot s holding row s / SPR, chunk s % SPR of the
+    // padded layout (pad slots and the slack past the last row get harmless
+    // copies); a wave past the last instruction repeats it.
+    auto dma = [&](__amdgpu_buffer_rsrc_t rsrc, uint16_t* dst, int stride, int q0) {
+        const int spr = stride / 8;
+        const int ninst = (kQT * spr + 63) / 64;
+#pragma unroll
+        for (int i = 0; i < (kQT * (D + kTP) / 8 / 64 + kKW) / kKW; ++i) {
+            const int j = min(wave + kKW * i, ninst - 1);  // wave-uniform
+            const int slot = 64 * j + lane;
+            const int rr = slot / spr;
+            const int ch = slot - rr * spr;
+            const int col = (ch < CPR ? ch : 0) * 8;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void*)(dst + 512 * j), 16,
+                ((q0 + rr) * D + col) * 2, 0, 0, 0);
+        }
     };
     auto tile_q0 = [&](int it) { return qstart + (it - (it / ntq) * ntq) * kQT; };
-    auto gload = [&](int it, Pair& r) {  // pairs past the last repeat it (never used)
+    auto gload = [&](int it, int P, Pair& r) {  // pairs past the last repeat it (never used)
         it = min(it, niter - 1);
         const int hh = it / ntq;
         const int q0 = qstart + (it - hh * ntq) * kQT;
@@ -184,14 +210,10 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             const_cast<uint16_t*>(q + qoff * D), (short)0, Nq * D * 2, 0x00020000);
         const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(do16 + qoff * D), (short)0, Nq * D * 2, 0x00020000);
-#pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            const int c = (tid + NT * i) % NCH;
-            const int rr = c / CPR;
-            const int col = (c - rr * CPR) * 8;
-            r.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, ((q0 + rr) * D + col) * 2, 0, 0);
-            r.o[i] = __builtin_amdgcn_raw_buffer_load_b128(ro, ((q0 + rr) * D + col) * 2, 0, 0);
-        }
+        dma(rq, Qr(P), RS, q0);
+        dma(ro, Or(P), RS, q0);
+        dma(rq, Qt(P), TS, q0);
+        dma(ro, Ot(P), TS, q0);
         // every thread fetches the statistics of row tid % 32 (the same value
         // for the same slot, so the stores need no branch).  Buffer loads
         // bounded to this head's rows: rows past Nq read 0, and their lse
@@ -205,25 +227,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
               (qr < Nq ? 0.f : INFINITY);
         r.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, qr * 4, 0, 0));
     };
-    auto store_rows = [&](int buf, const Pair& r) {
-#pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            const int c = (tid + NT * i) % NCH;
-            const int rr = c / CPR;
-            const int col = (c - rr * CPR) * 8;
-            *reinterpret_cast<u32x4*>(&Qr[buf][rr * RS + col]) = r.q[i];
-            *reinterpret_cast<u32x4*>(&Or[buf][rr * RS + col]) = r.o[i];
-        }
-    };
-    auto store_tr = [&](int buf, const Pair& r) {
-#pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            const int c = (tid + NT * i) % NCH;
-            const int rr = c / CPR;
-            const int col = (c - rr * CPR) * 8;
-            *reinterpret_cast<u32x4*>(&Qt[buf][rr * TS + col]) = r.q[i];
-            *reinterpret_cast<u32x4*>(&Ot[buf][rr * TS + col]) = r.o[i];
-        }
+    auto store_stats = [&](int buf, const Pair& r) {
         Ls[buf][l32] = r.l;
         Dsh[buf][l32] = r.d;
     };
@@ -232,8 +236,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     auto scores = [&](int buf, f32x16& sa, f32x16& pa) {
         sa = f32x16{};
         pa = f32x16{};
-        const uint16_t* Qb = Qr[buf];
-        const uint16_t* Ob = Or[buf];
+        const uint16_t* Qb = Qr(buf);
+        const uint16_t* Ob = Or(buf);
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
             const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&Qb[l32 * RS + 16 * s + 8 * half]);
@@ -265,8 +269,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             dw[j >> 1][2 * (j & 1)] = pack_bf16x2(ds[0], ds[1]);
             dw[j >> 1][2 * (j & 1) + 1] = pack_bf16x2(ds[2], ds[3]);
         }
-        const uint16_t* Qb = Qt[buf];
-        const uint16_t* Ob = Ot[buf];
+        const uint16_t* Qb = Qt(buf);
+        const uint16_t* Ob = Ot(buf);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const u32x4 p4 = {pw[ks][0], pw[ks][1], pw[ks][2], pw[ks][3]};
@@ -284,22 +288,22 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     };
 
     // prologue: pair 0 in buffer 0
+    auto dma_wait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
     Pair X;
-    gload(0, X);
-    store_rows(0, X);
-    store_tr(0, X);
+    gload(0, 0, X);
+    store_stats(0, X);
+    dma_wait();
     __syncthreads();
     auto step = [&](int it, int P) {
-        gload(it + 1, X);
-        // keep the loads here, a whole pair ahead of their LDS stores (the
-        // scheduler would otherwise sink them next to their use)
+        // buffer P^1 held pair it-1, last read before the previous barrier
+        gload(it + 1, P ^ 1, X);
+        // keep the loads here, a whole pair ahead of their use
         __builtin_amdgcn_sched_barrier(0);
         f32x16 sc, pc;
         scores(P, sc, pc);
         accumulate(P, tile_q0(it), sc, pc);
-        // buffer P^1 held pair it-1, last read before the previous barrier
-        store_rows(P ^ 1, X);
-        store_tr(P ^ 1, X);
+        store_stats(P ^ 1, X);
+        dma_wait();
         __syncthreads();
     };
     int it = 0;
