@@ -99,7 +99,7 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     constexpr int KSD = D + 8;          // K row stride in LDS: 4 banks mod 64
     constexpr int NW = kSplitWaves;
     __shared__ __attribute__((aligned(16))) uint16_t Vl[NW][kBatch * VSD];
-    __shared__ float cm[NW][16], cl[NW][16], cr[NW][16];
+    __shared__ float cm[NW][16], cl[NW][16], cr[NW][16], cw[NW][16];
     __shared__ float co[NW][GP][D];
 
     const int tid = threadIdx.x;
@@ -327,27 +327,38 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         }
     }
     __syncthreads();
-    for (int i = tid; i < nh * D; i += NW * 64) {
-        const int h = i / D;
-        const int d = i - h * D;
+    // per column: the common max, each wave's weight divided by the merged
+    // denominator, and the chunk's lse (one thread per column)
+    if (tid < nh) {
+        const int h = tid;
         float M = cm[0][h];
 #pragma unroll
         for (int w = 1; w < NW; ++w) M = fmaxf(M, cm[w][h]);
-        float acc = 0.f, rs = 0.f, ls = 0.f;
+        float f[NW];
+        float rs = 0.f, ls = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             // 0 for a wave without keys for this column
-            const float f = cm[w][h] == -INFINITY ? 0.f : fast_exp2(cm[w][h] - M);
-            acc = fmaf(f, co[w][h][d], acc);
-            rs = fmaf(f, cr[w][h], rs);
-            ls = fmaf(f, cl[w][h], ls);
+            f[w] = cm[w][h] == -INFINITY ? 0.f : fast_exp2(cm[w][h] - M);
+            rs = fmaf(f[w], cr[w][h], rs);
+            ls = fmaf(f[w], cl[w][h], ls);
         }
         // a column with no key in this chunk (a new token before it) gets the
-        // empty state; the merge kernel never reads it
+        // empty state (weights 0, lse -inf); the merge kernel never reads it
         const bool empty = M == -INFINITY;
-        const size_t row = (row0 + h) * nchunks + c;
-        ws_o[row * D + d] = empty ? 0.f : acc / rs;
-        if (d == 0) ws_lse[row] = empty ? -INFINITY : M + fast_log2(ls);
+        const float inv = empty ? 0.f : 1.f / rs;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) cw[w][h] = f[w] * inv;
+        ws_lse[(row0 + h) * nchunks + c] = empty ? -INFINITY : M + fast_log2(ls);
+    }
+    __syncthreads();
+    for (int i = tid; i < nh * D; i += NW * 64) {
+        const int h = i / D;
+        const int d = i - h * D;
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) acc = fmaf(cw[w][h], co[w][h][d], acc);
+        ws_o[((row0 + h) * nchunks + c) * D + d] = acc;
     }
 }
 
