@@ -260,6 +260,10 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         //      this tile's weights on the vector ALU, then P V.
         gload(pk, rk, key0 + 2 * kBc);  // K(t+2) in flight (zeros past the end)
         gload(pv, rv, key0 + kBc);      // V(t+1) in flight
+        // keep the loads here: left to itself the scheduler moves them down
+        // to their LDS stores, and every tile then waits for a full memory
+        // round trip
+        __builtin_amdgcn_sched_barrier(0);
         qk(Ks[(t + 1) & 1], sn_);
         const uint16_t* Vt = Vs[t & 1];
         float psum = 0.f;
