@@ -215,6 +215,8 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     lstore(pk, Ks[1], KS);
     __syncthreads();
     qk(Ks[0], scur);
+    // K(0) is overwritten by the first iteration: every wave has read it first
+    __syncthreads();
 
     // One tile iteration; the loop below alternates the two score buffers so
     // no copy is needed between iterations.
