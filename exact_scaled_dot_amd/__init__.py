@@ -119,10 +119,27 @@ def _check(fn, code):
 
 
 def _need_cuda_contig(name, t):
+    import torch
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    # kernels run on the current device and its current stream
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, but the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
+
+
+def _check_out(name, t, shape, dtype):
+    """A caller-supplied output or workspace: the kernels write exactly `shape`
+    elements of `dtype` from its first element, so anything else is rejected."""
+    if t is None:
+        return
+    _need_cuda_contig(name, t)
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
 def fwd_workspace_bytes(B, Hkv, Nk, d, rope_base, dtype_code) -> int:
@@ -156,6 +173,9 @@ def fwd(q, k, v, causal: bool, scale=None, rope_base: float = 0.0, out=None, lse
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    _check_out("out", out, (B, Hq, Nq, d), torch.float32)
+    _check_out("lse", lse, (B, Hq, Nq), torch.float32)
+    _check_out("workspace", workspace, None, torch.uint8)
     if out is None:
         out = torch.empty((B, Hq, Nq, d), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
@@ -200,6 +220,10 @@ def bwd(q, k, v, o, lse, dout, causal: bool, scale=None, rope_base: float = 0.0,
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    _check_out("dq", dq, (B, Hq, Nq, d), torch.float32)
+    _check_out("dk", dk, (B, Hkv, Nk, d), torch.float32)
+    _check_out("dv", dv, (B, Hkv, Nk, d), torch.float32)
+    _check_out("workspace", workspace, None, torch.uint8)
     if dq is None:
         dq = torch.empty((B, Hq, Nq, d), dtype=torch.float32, device=q.device)
     if dk is None:
@@ -233,6 +257,9 @@ def decode(q, k_cache, v_cache, seq_lens, scale=None, out=None, lse=None, worksp
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    _check_out("out", out, (B, Hq, d), torch.float32)
+    _check_out("lse", lse, (B, Hq), torch.float32)
+    _check_out("workspace", workspace, None, torch.uint8)
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
@@ -264,6 +291,9 @@ def decode_multi(q, k_cache, v_cache, seq_lens, scale=None, rope_base: float = 0
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    _check_out("out", out, (B, Hq, T, d), torch.float32)
+    _check_out("lse", lse, (B, Hq, T), torch.float32)
+    _check_out("workspace", workspace, None, torch.uint8)
     if out is None:
         out = torch.empty((B, Hq, T, d), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
@@ -302,6 +332,9 @@ def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale=None, rope_base
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    _check_out("out", out, (B, Hq, T, d), torch.float32)
+    _check_out("lse", lse, (B, Hq, T), torch.float32)
+    _check_out("workspace", workspace, None, torch.uint8)
     if out is None:
         out = torch.empty((B, Hq, T, d), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
@@ -323,6 +356,7 @@ def rope_apply(x, rope_base: float, pos_offset: int = 0, out=None):
     L = lib()
     _need_cuda_contig("x", x)
     B, H, N, d = x.shape
+    _check_out("out", out, (B, H, N, d), x.dtype)
     if out is None:
         out = torch.empty_like(x)
     _check("attn_rope_apply", L.attn_rope_apply(_ptr(x), _ptr(out), B, H, N, d, int(pos_offset),
