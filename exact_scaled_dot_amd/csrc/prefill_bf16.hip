@@ -11,15 +11,17 @@
 // comparison table in "Transformer Architecture Breakdown", section 4.3 names.
 //
 // gfx950 mapping
-//   * workgroup = 8 waves (two per SIMD); each wave owns 32 query rows of one
-//     query head.  The waves of a workgroup cover the query heads of one KV head
-//     (GQA group) and share every K/V tile, so a tile is read from memory once
-//     per group of heads.
-//   * K/V tiles of 64 keys are double-buffered in LDS, with K one tile ahead
-//     of V: iteration t forms the scores of tile t+1 on the matrix cores while
-//     the vector ALU runs the softmax of tile t, then accumulates P V of tile t.
-//     The tiles two (K) and one (V) ahead are loaded into registers during the
-//     iteration and stored afterwards, with one barrier per tile.
+//   * workgroup = 12 waves at d = 128, three per SIMD (8 at d = 64); each wave
+//     owns 32 query rows of one query head.  The waves of a workgroup cover query heads of one KV
+//     head (GQA group) and share every K/V tile, so a tile is read from memory
+//     once per group of heads.  Each wave runs a plain sequence per 32 keys
+//     (scores, mask, max, rescale, weights, P V); with three waves on a SIMD the
+//     hardware overlaps one wave's matrix products with another's vector work,
+//     and 168 registers per wave leave room for exactly three.
+//   * K/V tiles of 64 keys are double-buffered in LDS.  The tiles arrive
+//     straight from memory (buffer_load ... lds) while the previous tile is
+//     used, with one barrier per tile; each tile takes two online-softmax
+//     updates of 32 keys.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: in the 32x32 accumulator a lane
 //     holds one query (column) and 16 keys, so the row max and sum need one
 //     exchange between the two 32-lane halves.
@@ -29,18 +31,19 @@
 //     read with the gfx950 transposing LDS load (ds_read_b64_tr_b16).
 //   * softmax in the exp2 domain: p = 2^(s * scale * log2(e) - m) with one FMA
 //     and one v_exp_f32 per score.  The reference max m of a row moves only when
-//     the row max exceeds it by more than 8 (a factor 2^8), so most tiles skip
+//     the row max exceeds it by more than 8 (a factor 2^8), so most updates skip
 //     the rescale of O and l; O and l always share one reference, so the result
 //     is the same exact recurrence.  O is divided by the sum of the bf16-rounded
 //     weights that entered the P V product (a true convex combination of V
 //     rows); the logsumexp uses the fp32 sum.
-//   * causal: a workgroup stops at the last tile its rows can see, the element
-//     mask is applied only on tiles that cross a wave's diagonal or the end of
-//     K, and heavy row blocks are launched first.
+//   * causal: a workgroup stops at the last tile its rows can see, a wave skips
+//     32-key blocks past its last row, the element mask is applied only on
+//     blocks that cross a wave's diagonal or the end of K, and heavy row blocks
+//     are launched first.
 //   * sliding window w ("Attention mechanisms: from alignment to efficient long
 //     context", section 11; causal only): a query at position p sees keys
 //     p-w+1 .. p, so a workgroup also starts at the first tile its first row
-//     can see, and tiles that cross a wave's lower window edge are masked too.
+//     can see, and blocks that cross a wave's lower window edge are masked too.
 //     Work per row is then O(w) instead of O(N).
 
 #include "device_common.h"
@@ -52,7 +55,11 @@ namespace {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 8;   // 2 per SIMD
+// waves per workgroup: three per SIMD at d = 128 (168 registers each); at
+// d = 64 two per SIMD, so that a workgroup of one query head covers 256 rows
+// and short sequences still give many workgroups
+template <int D>
+constexpr int waves_for() { return D == 128 ? 12 : 8; }
 constexpr int kRows = 32;   // query rows per wave
 constexpr int kBc = 64;     // keys per tile
 constexpr int kKPad = 8;    // K rows: stride = 4 banks mod 64, conflict-free 16-byte operand reads
@@ -73,24 +80,29 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
 }
 
 template <int D, bool CAUSAL, bool ROPE, bool WINDOW>
-__global__ void __launch_bounds__(kWaves * 64, 1)
+__global__ void __launch_bounds__(waves_for<D>() * 64, 1)
 prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, float* __restrict__ o,
                     float* __restrict__ lse, int B, int Hq, int Hkv, int Nq, int Nk,
                     float scale_log2, const double2* __restrict__ tab, int hpw, int wph,
                     int nchunks, int nrb, int win) {
     static_assert(!WINDOW || CAUSAL, "the sliding window is built for causal attention");
+    constexpr int kWaves = waves_for<D>();
     constexpr int NT = kWaves * 64;
     constexpr int KS = D + kKPad;       // K row stride in LDS (elements)
     constexpr int VS = D + kVPad;       // V row stride in LDS (elements)
     constexpr int CPR = D / 8;          // 16-byte chunks per row
-    constexpr int LPT = kBc * CPR / NT; // chunks of K (and of V) per thread per tile
-    static_assert(LPT >= 1 && (kBc * CPR) % NT == 0, "tile/thread mismatch");
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBc * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBc * VS];
+    // one object per buffer, so the compiler knows that the tile loads into
+    // one buffer do not alias the reads from the other
+    __shared__ __attribute__((aligned(16))) uint16_t Ks0[kBc * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks1[kBc * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs0[kBc * VS];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs1[kBc * VS];
+    auto kbuf = [&](int P) -> uint16_t* { return P ? Ks1 : Ks0; };
+    auto vbuf = [&](int P) -> uint16_t* { return P ? Vs1 : Vs0; };
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int half = lane >> 5;
@@ -130,37 +142,35 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const uint16_t* kbase = k + ((size_t)b * Hkv + g) * (size_t)Nk * D;
     const uint16_t* vbase = v + ((size_t)b * Hkv + g) * (size_t)Nk * D;
 
-    // ---- tile loaders: global -> registers -> LDS (row-major, padded).
-    //      K runs one tile ahead of V: while tile t's softmax runs, the scores of
-    //      tile t+1 are already being formed on the matrix cores.  Buffer loads:
-    //      the scalar resource spans this head's Nk rows, so rows past the end
-    //      read as zeros and no load needs a branch.
+    // ---- tile loads: memory straight into LDS (buffer_load ... lds).  One
+    //      instruction writes lane L's 16 bytes at its LDS base + 16 L, so a
+    //      padded tile is filled in 16-byte slots, slot s holding row s / SPR,
+    //      chunk s % SPR; the pad slot of a row receives a copy of its first
+    //      chunk.  The scalar resource spans this head's Nk rows, so rows past
+    //      the end read as zeros and no load needs a branch.
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(kbase), (short)0, Nk * D * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(vbase), (short)0, Nk * D * 2, 0x00020000);
-    u32x4 pk[LPT], pv[LPT];
-    auto gload = [&](u32x4 (&dst)[LPT], __amdgpu_buffer_rsrc_t rsrc, int key0) {
+    auto dma = [&](__amdgpu_buffer_rsrc_t rsrc, uint16_t* dstbuf, int stride, int key0) {
+        static_assert(kBc == 64, "one load instruction per 64 slots = per slot column");
+        const int spr = stride / 8;  // 16-byte slots per padded row
+        const int ninst = spr;       // kBc rows x spr slots / 64 lanes
+        // no branch: a wave past the last instruction repeats it, writing the
+        // same bytes to the same slots
 #pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            const int c = tid + NT * i;
-            const int r = c / CPR;
-            const int col = (c - r * CPR) * 8;
-            dst[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, ((key0 + r) * D + col) * 2, 0, 0);
+        for (int i = 0; i < (ninst + kWaves - 1) / kWaves; ++i) {
+            const int j = min(wave + kWaves * i, ninst - 1);  // wave-uniform
+            const int slot = 64 * j + lane;
+            const int r = slot / spr;
+            const int ch = slot - r * spr;
+            const int col = (ch < CPR ? ch : 0) * 8;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void*)(dstbuf + 512 * j), 16,
+                ((key0 + r) * D + col) * 2, 0, 0, 0);
         }
     };
-    auto lstore = [&](const u32x4 (&src)[LPT], uint16_t* dstbuf, int stride) {
-#pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            const int c = tid + NT * i;
-            const int r = c / CPR;
-            const int col = (c - r * CPR) * 8;
-            *reinterpret_cast<u32x4*>(&dstbuf[r * stride + col]) = src[i];
-        }
-    };
-
-    gload(pk, rk, kbeg);
-    gload(pv, rv, kbeg);
+    auto dma_wait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
 
     // ---- Q fragment (B operand of S^T = K Q^T): query l32, d = 16s + 8*half .. +7
     bf16x8 qf[D / 16];
@@ -194,55 +204,30 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const int vcol_in = 16 * (grp & 1) + 4 * (w16 & 3);
     const int vkey_h = 4 * (grp >> 1);  // = 4 * half
 
-    // S^T = K Q^T for one 64-key tile held in LDS
-    auto qk = [&](const uint16_t* Kt, f32x16 (&sacc)[2]) {
+    // One online-softmax update over 32 keys held in LDS (rows Kt, Vt):
+    // S^T = K Q^T, mask, row max, rare rescale, weights, O^T += V^T P^T.
+    auto half_update = [&](const uint16_t* Kt, const uint16_t* Vt, int key0) {
+        f32x16 sc = f32x16{};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            sacc[kb] = f32x16{};
-#pragma unroll
-            for (int s = 0; s < D / 16; ++s) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kt[(kb * 32 + l32) * KS + 16 * s + 8 * half]);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
-            }
+        for (int s = 0; s < D / 16; ++s) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kt[l32 * KS + 16 * s + 8 * half]);
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sc, 0, 0, 0);
         }
-    };
-
-    // prologue: K(0), V(0) and K(1) in LDS, S(0) formed
-    f32x16 scur[2], snext[2];
-    lstore(pk, Ks[0], KS);
-    lstore(pv, Vs[0], VS);
-    gload(pk, rk, kbeg + kBc);
-    lstore(pk, Ks[1], KS);
-    __syncthreads();
-    qk(Ks[0], scur);
-    // K(0) is overwritten by the first iteration: every wave has read it first
-    __syncthreads();
-
-    // One tile iteration; the loop below alternates the two score buffers so
-    // no copy is needed between iterations.
-    auto step = [&](int t, f32x16 (&sc_)[2], f32x16 (&sn_)[2]) {
-        const int key0 = kbeg + t * kBc;
-        // ---- short prologue (may branch): mask, row max, rare rescale
-        const bool need_mask = (key0 + kBc > Nk) || (CAUSAL && key0 + kBc - 1 > wave_first) ||
+        const bool need_mask = (key0 + 32 > Nk) || (CAUSAL && key0 + 31 > wave_first) ||
                                (WINDOW && key0 < wave_lo);
         if (need_mask) {
             keep_branch();
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-                    const bool vis = (key < Nk) && (!CAUSAL || key <= qpos) &&
-                                     (!WINDOW || key > qpos - win);
-                    sc_[kb][i] = vis ? sc_[kb][i] : -INFINITY;
-                }
+            for (int i = 0; i < 16; ++i) {
+                const int key = key0 + 8 * (i >> 2) + 4 * half + (i & 3);
+                const bool vis = (key < Nk) && (!CAUSAL || key <= qpos) &&
+                                 (!WINDOW || key > qpos - win);
+                sc[i] = vis ? sc[i] : -INFINITY;
             }
         }
         float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sc_[kb][i], sc_[kb][i + 1]));
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sc[i], sc[i + 1]));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_cand = mx * scale_log2;
         const bool grow = m_cand > m_run + kLazy;
@@ -257,69 +242,66 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             m_run = m_new;
         }
         const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
-
-        // ---- main block, no branches: next tile's scores on the matrix cores,
-        //      this tile's weights on the vector ALU, then P V.
-        gload(pk, rk, key0 + 2 * kBc);  // K(t+2) in flight (zeros past the end)
-        gload(pv, rv, key0 + kBc);      // V(t+1) in flight
-        // keep the loads here: left to itself the scheduler moves them down
-        // to their LDS stores, and every tile then waits for a full memory
-        // round trip
-        __builtin_amdgcn_sched_barrier(0);
-        qk(Ks[(t + 1) & 1], sn_);
-        const uint16_t* Vt = Vs[t & 1];
         float psum = 0.f;
-        uint4 pw[2][2];
+        uint4 pw[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int ss = 0; ss < 2; ++ss) {
+            float p[8];
 #pragma unroll
-            for (int ss = 0; ss < 2; ++ss) {
-                float p[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    p[e] = fast_exp2(fmaf(sc_[kb][8 * ss + e], scale_log2, neg_m));
-                    psum += p[e];
-                }
-                pw[kb][ss].x = pack_bf16x2(p[0], p[1]);
-                pw[kb][ss].y = pack_bf16x2(p[2], p[3]);
-                pw[kb][ss].z = pack_bf16x2(p[4], p[5]);
-                pw[kb][ss].w = pack_bf16x2(p[6], p[7]);
-                r_run = sum_bf16x2(pw[kb][ss].x, r_run);
-                r_run = sum_bf16x2(pw[kb][ss].y, r_run);
-                r_run = sum_bf16x2(pw[kb][ss].z, r_run);
-                r_run = sum_bf16x2(pw[kb][ss].w, r_run);
+            for (int e = 0; e < 8; ++e) {
+                p[e] = fast_exp2(fmaf(sc[8 * ss + e], scale_log2, neg_m));
+                psum += p[e];
             }
+            pw[ss].x = pack_bf16x2(p[0], p[1]);
+            pw[ss].y = pack_bf16x2(p[2], p[3]);
+            pw[ss].z = pack_bf16x2(p[4], p[5]);
+            pw[ss].w = pack_bf16x2(p[6], p[7]);
+            r_run = sum_bf16x2(pw[ss].x, r_run);
+            r_run = sum_bf16x2(pw[ss].y, r_run);
+            r_run = sum_bf16x2(pw[ss].z, r_run);
+            r_run = sum_bf16x2(pw[ss].w, r_run);
         }
         l_run += psum;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int ss = 0; ss < 2; ++ss) {
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[ss]);
+            const int kbase_l = 16 * ss + vkey_h + vrow_in;
 #pragma unroll
-            for (int ss = 0; ss < 2; ++ss) {
-                const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kb][ss]);
-                const int kbase_l = kb * 32 + 16 * ss + vkey_h + vrow_in;
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const uint16_t* vp = Vt + kbase_l * VS + 32 * db + vcol_in;
-                    const s16x4 lo = lds_read_tr(vp);
-                    const s16x4 hi = lds_read_tr(vp + 8 * VS);
-                    const bf16x8 a = __builtin_bit_cast(
-                        bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
-                }
+            for (int db = 0; db < D / 32; ++db) {
+                const uint16_t* vp = Vt + kbase_l * VS + 32 * db + vcol_in;
+                const s16x4 lo = lds_read_tr(vp);
+                const s16x4 hi = lds_read_tr(vp + 8 * VS);
+                const bf16x8 a = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
             }
         }
-        // K(t+2) replaces K(t), V(t+1) replaces V(t-1): both last read before
-        // the previous barrier
-        lstore(pk, Ks[t & 1], KS);
-        lstore(pv, Vs[(t + 1) & 1], VS);
+    };
+    // Tile t (64 keys in buffer P = t & 1, a constant at every call): two
+    // updates, while K/V(t+1) arrive in the other buffer.
+    auto step = [&](int t, int P) {
+        const int key0 = kbeg + t * kBc;
+        // K/V(t+1) replace K/V(t-1), last read before the previous barrier
+        dma(rk, kbuf(P ^ 1), KS, key0 + kBc);
+        dma(rv, vbuf(P ^ 1), VS, key0 + kBc);
+        half_update(kbuf(P), vbuf(P), key0);
+        // the second half is skipped when no key of it is visible to any row of
+        // the wave (causal tail, end of K)
+        if (key0 + 32 < Nk && (!CAUSAL || key0 + 32 <= wave_last))
+            half_update(kbuf(P) + 32 * KS, vbuf(P) + 32 * VS, key0 + 32);
+        dma_wait();
         __syncthreads();
     };
+    dma(rk, Ks0, KS, kbeg);
+    dma(rv, Vs0, VS, kbeg);
+    dma_wait();
+    __syncthreads();
     int t = 0;
     for (; t + 1 < ntiles; t += 2) {
-        step(t, scur, snext);
-        step(t + 1, snext, scur);
+        step(t, 0);
+        step(t + 1, 1);
     }
-    if (t < ntiles) step(t, scur, snext);
+    if (t < ntiles) step(t, 0);
 
     if (!active || qi >= Nq) return;
     // O is the convex combination with the weights the MFMA actually used (their
@@ -345,7 +327,12 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 template <int D, bool CAUSAL, bool ROPE, bool WINDOW>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     const int G = a.Hq / a.Hkv;
-    const int hpw = G < kWaves ? G : kWaves;          // query heads per workgroup
+    // query heads per workgroup: the largest common divisor of the group size
+    // and the wave count, so every wave of a workgroup has rows to work on
+    int hpw = 1;
+    constexpr int kWaves = waves_for<D>();
+    for (int c = 1; c <= kWaves; ++c)
+        if (kWaves % c == 0 && G % c == 0) hpw = c;
     const int wph = kWaves / hpw;                      // waves per head
     const int nchunks = (G + hpw - 1) / hpw;
     const int rows_per_wg = wph * kRows;
