@@ -228,7 +228,17 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sc[i], sc[i + 1]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        {
+            // the other half's max: v_permlane32_swap gives lanes 0-31 (r[0])
+            // and lanes 32-63 (r[1]) in both halves, with no LDS round trip
+            const unsigned u = __builtin_bit_cast(unsigned, mx);
+            const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+            // opaque to the optimiser: left visible, the max of the two results
+            // is folded into the first one alone
+            unsigned lo = r[0], hi = r[1];
+            asm volatile("" : "+v"(lo), "+v"(hi));
+            mx = fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
+        }
         const float m_cand = mx * scale_log2;
         const bool grow = m_cand > m_run + kLazy;
         if (__ballot(grow)) {
