@@ -253,6 +253,11 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         }
         const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
         float psum = 0.f;
+        // the weights are the one stretch of pure vector work: raising the
+        // wave's issue priority here lets it finish them while the other waves
+        // of the SIMD keep the matrix cores fed (measured +1.5%; raising it
+        // around the products instead loses 3.5%)
+        __builtin_amdgcn_s_setprio(1);
         uint4 pw[2];
 #pragma unroll
         for (int ss = 0; ss < 2; ++ss) {
@@ -272,6 +277,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             r_run = sum_bf16x2(pw[ss].w, r_run);
         }
         l_run += psum;
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int ss = 0; ss < 2; ++ss) {
             const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[ss]);
