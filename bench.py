@@ -37,6 +37,7 @@ import workloads as W  # noqa: E402
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
+CLOCK_RECORD = os.path.join(ROOT, "profiles", "clock.json")
 CSRC = os.path.join(ROOT, "exact_scaled_dot_amd", "csrc")
 
 
@@ -69,6 +70,25 @@ def recorded_traffic(kernel: str):
         return None
     cal = rec["calibration"]
     return (k["fetch_kib"] * cal["fetch_factor"] + k["write_kib"] * cal["write_factor"]) * 1024.0
+
+
+def recorded_clock(kernel: str):
+    """Shader clock (GHz) under ``kernel`` from the committed counter record:
+    GPU-active cycles per dispatch (from MfmaUtil = MFMA busy cycles / (active
+    cycles x SIMDs)) over the dispatch time of the same profiled run; None when
+    the record is missing or was taken on other kernel sources."""
+    try:
+        import json as _json
+        with open(CLOCK_RECORD) as f:
+            rec = _json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if not k else float(k["sclk_ghz"])
+
+
 METRIC = "attn fwd TFLOP/s (causal GQA N=8192 d=128 bf16) + decode HBM GB/s"
 
 
@@ -393,6 +413,7 @@ def main():
     # not part of it
     wall -= float(np.sum(rope_ms)) * 1e-3 if do_pf else 0.0
     pf_traffic = recorded_traffic("prefill_bf16_kernel<128, true, true, false>")
+    pf_sclk = recorded_clock("prefill_bf16_kernel<128, true, true, false>")
     dec_split = recorded_traffic("decode_split_kernel<128, 4, false>")
     dec_merge = recorded_traffic("decode_merge_kernel<128>")
     dec_traffic = dec_split + dec_merge if dec_split is not None and dec_merge is not None else None
@@ -422,6 +443,11 @@ def main():
             "bound": "mfma", "achieved": kern_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": (kern_tflops / PEAK_BF16_TFLOPS) if kern_tflops else None,
             "traffic": pf_traffic,
+            # the clock sags under this load: the fraction of the peak at the
+            # shader clock the counters measured under this kernel
+            "sclk_ghz": pf_sclk,
+            "frac_at_sclk": (kern_tflops / (PEAK_BF16_TFLOPS * pf_sclk / 2.4))
+                            if (kern_tflops and pf_sclk) else None,
         },
         "decode": {
             "value": gbs, "unit": "GB/s",
