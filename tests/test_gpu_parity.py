@@ -74,6 +74,20 @@ def test_head_sharing(Hq, Hkv, dtype):
     check(o, lse, ro, rl, dtype, f"Hq={Hq} Hkv={Hkv} {dtype}")
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(10, 2), (12, 2), (7, 1), (24, 2), (32, 2)])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_group_sizes_split_over_workgroups(Hq, Hkv, d, causal):
+    """Group sizes 5, 6, 7, 12 and 16: the heads of one KV head are spread over
+    one or several workgroups (a common divisor of the group size and the wave
+    count per workgroup), with a ragged row tail."""
+    q, k, v = _small_inputs(7150 + Hq * 10 + Hkv + d, 1, Hq, Hkv, 77, 140, d, "bf16")
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _run_fwd(q, k, v, "bf16", causal, scale, 0.0)
+    ro, rl = oa.attention(q, k, v, causal=causal, scale=scale, dtype="bf16")
+    check(o, lse, ro, rl, "bf16", f"Hq={Hq} Hkv={Hkv} d={d} causal={causal}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("base", [10000.0, 500000.0, 10.0])
 @pytest.mark.parametrize("d", [64, 128])
