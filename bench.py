@@ -173,7 +173,7 @@ def cpu_baseline(w3, w4, budget_s=20.0):
     }
 
 
-EXTRA = (("c2", 0), ("c5", 0), ("c3", 4096), ("c5", 4096))
+EXTRA = (("mha_d64_n2048", 0), ("gqa_rope_n32768", 0), ("gqa_rope_n8192", 4096), ("gqa_rope_n32768", 4096))
 
 
 def extra_prefill(torch, esd, stream, reps=5):
@@ -331,15 +331,15 @@ def main():
         print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "copies": 3}))
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
     import torch
     import exact_scaled_dot_amd as esd
 
-    w3 = W.WORKLOADS["c3"]
-    w4 = W.WORKLOADS["c4"]
+    w3 = W.WORKLOADS["gqa_rope_n8192"]
+    w4 = W.WORKLOADS["decode_b32"]
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
 
@@ -471,7 +471,7 @@ def main():
         del dq, dk, dv, o3, l3, ws3, kr3, dqd, o4, l4, ws4
         torch.cuda.empty_cache()
         rec["extra"] = extra_prefill(torch, esd, stream)
-        rec["extra"]["c3_backward"] = extra_backward(torch, esd, stream, w3)
+        rec["extra"]["gqa_rope_n8192_backward"] = extra_backward(torch, esd, stream, w3)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(w3, w4)

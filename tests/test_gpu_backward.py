@@ -115,10 +115,10 @@ def test_bwd_gqa_n8192_sampled():
     """Causal GQA + RoPE 1e4, B=2 Hq=32 Hkv=8 N=8192 d=128: dQ on sampled query
     rows of the four heads of one KV head, dK and dV on sampled key rows."""
     import torch
-    w = W.WORKLOADS["c3"]
+    w = W.WORKLOADS["gqa_rope_n8192"]
     q, k, v = W.fwd_inputs(w)
     do = W.normal((w.B, w.Hq, w.Nq, w.d), 11500, 1.0, "f32")
-    say(f"bwd c3 shape: {w.note}")
+    say(f"bwd gqa_rope_n8192 shape: {w.note}")
     got = _run(q, k, v, do, True, w.scale, w.rope_base)
     N = w.Nq
     rows = np.unique(np.concatenate([[0, 1, 31, 32, 63, 64, 127, 128, N // 2, N - 129, N - 33,
@@ -128,8 +128,8 @@ def test_bwd_gqa_n8192_sampled():
     sq, sk, sv = oa.attention_bwd_rows(q, k, v, do, b, g, rows, rows, causal=True, scale=w.scale,
                                        rope_base=w.rope_base, dtype="bf16")
     G = w.Hq // w.Hkv
-    _grad_check(got[0][b, g * G:(g + 1) * G][:, rows], sq, f"bwd c3 dq ({len(rows)} rows x {G} heads)")
-    _grad_check(got[1][b, g, rows], sk, f"bwd c3 dk ({len(rows)} rows)")
-    _grad_check(got[2][b, g, rows], sv, f"bwd c3 dv ({len(rows)} rows)")
+    _grad_check(got[0][b, g * G:(g + 1) * G][:, rows], sq, f"bwd gqa_rope_n8192 dq ({len(rows)} rows x {G} heads)")
+    _grad_check(got[1][b, g, rows], sk, f"bwd gqa_rope_n8192 dk ({len(rows)} rows)")
+    _grad_check(got[2][b, g, rows], sv, f"bwd gqa_rope_n8192 dv ({len(rows)} rows)")
     del got
     torch.cuda.empty_cache()

@@ -88,7 +88,7 @@ def test_bwd_rejects_bad_gradients():
 
 def test_decode_rejects_bad_outputs():
     import torch
-    w = W.WORKLOADS["c4"]
+    w = W.WORKLOADS["decode_b32"]
     lens = np.array([5, 300, 1500], dtype=np.int32)
     q, kc, vc = W.decode_inputs(w, lens, Hq=8, Hkv=2, d=64, max_len=1600, seed_base=12100)
     f32 = dict(dtype=torch.float32, device="cuda")
@@ -110,7 +110,7 @@ def test_decode_rejects_bad_outputs():
 
 def test_decode_multi_rejects_wrong_token_count():
     import torch
-    w = W.WORKLOADS["c4"]
+    w = W.WORKLOADS["decode_b32"]
     lens = np.array([40, 300], dtype=np.int32)
     _, kc, vc = W.decode_inputs(w, lens, Hq=8, Hkv=2, d=64, max_len=512, seed_base=12200)
     q = W.normal((2, 8, 2, 64), 12207, 1.0, "bf16")

@@ -36,7 +36,7 @@ def _gpu():
 
 
 def _inputs(lens, Hq, Hkv, T, max_len, d, seed):
-    w = W.WORKLOADS["c4"]
+    w = W.WORKLOADS["decode_b32"]
     _, kc, vc = W.decode_inputs(w, lens, Hq=Hq, Hkv=Hkv, max_len=max_len, d=d, seed_base=seed)
     q = W.normal((len(lens), Hq, T, d), seed + 7, 1.0, "bf16")
     return q, kc, vc
@@ -97,14 +97,14 @@ def test_decode_multi_matches_prefill_rows():
     assert np.max(np.abs(o - host(of))) < 2e-2 and np.max(np.abs(lse - host(lf))) < 2e-3
 
 
-def test_decode_multi_speculative_c4_shape():
+def test_decode_multi_speculative_b32_shape():
     """The GQA decode batch (B=32, Hq=32, Hkv=8, d=128, lengths 1024..32768)
     verifying 4 drafted tokens per sequence: 16 queries per KV head, one pass."""
-    w = W.WORKLOADS["c4"]
+    w = W.WORKLOADS["decode_b32"]
     lens = W.decode_lens(w)
     _, kc, vc = W.decode_inputs(w, lens)
     q = W.normal((w.B, w.Hq, 4, w.d), 9700, 1.0, "bf16")
-    say(f"c4 shape with T=4: lens sum {lens.sum()}")
+    say(f"decode_b32 shape with T=4: lens sum {lens.sum()}")
     o, lse = _run(q, kc, vc, lens, w.scale)
     ro, rl = oa.decode_multi(q, kc, vc, lens, scale=w.scale, dtype="bf16")
-    _check_rows(o, lse, ro, rl, "decode_multi c4 T=4")
+    _check_rows(o, lse, ro, rl, "decode_multi decode_b32 T=4")

@@ -56,7 +56,7 @@ def _check_rows(o, lse, ro, rl, what):
 @pytest.mark.parametrize("Hq,Hkv,T", [(32, 8, 1), (32, 8, 4), (8, 8, 2), (16, 2, 1)])
 @pytest.mark.parametrize("d", [64, 128])
 def test_decode_paged_shapes(bs, Hq, Hkv, T, d):
-    w = W.WORKLOADS["c4"]
+    w = W.WORKLOADS["decode_b32"]
     q, kp, vp, table = W.paged_inputs(w, LENS, block_size=bs, T=T, Hq=Hq, Hkv=Hkv, d=d,
                                       seed_base=9800 + bs + Hq + T + d)
     scale = 1 / math.sqrt(d)
@@ -69,7 +69,7 @@ def test_decode_paged_shapes(bs, Hq, Hkv, T, d):
 def test_decode_paged_equals_contiguous(bs):
     """The same rows laid out contiguously give identical outputs."""
     import torch
-    w = W.WORKLOADS["c4"]
+    w = W.WORKLOADS["decode_b32"]
     q, kp, vp, table = W.paged_inputs(w, LENS, block_size=bs, T=3, Hq=32, Hkv=8, d=128,
                                       seed_base=9900 + bs)
     o, lse = _run(q, kp, vp, table, LENS, 0.0884, rope_base=10000.0)
@@ -86,7 +86,7 @@ def test_decode_paged_equals_contiguous(bs):
 
 
 def test_decode_paged_rope():
-    w = W.WORKLOADS["c4"]
+    w = W.WORKLOADS["decode_b32"]
     q, kp, vp, table = W.paged_inputs(w, LENS, block_size=16, T=2, Hq=16, Hkv=4, d=128,
                                       seed_base=9950)
     o, lse = _run(q, kp, vp, table, LENS, 0.0884, rope_base=10000.0)
@@ -95,13 +95,13 @@ def test_decode_paged_rope():
     _check_rows(o, lse, ro, rl, "paged rope")
 
 
-def test_decode_paged_c4_shape():
+def test_decode_paged_b32_shape():
     """The GQA decode batch (B=32, Hq=32, Hkv=8, d=128, lengths 1024..32768) in
     16-token blocks scattered over the pool."""
-    w = W.WORKLOADS["c4"]
+    w = W.WORKLOADS["decode_b32"]
     lens = W.decode_lens(w)
     q, kp, vp, table = W.paged_inputs(w, lens, block_size=16)
-    say(f"c4 paged: {kp.shape[0]} blocks of 16, lens sum {lens.sum()}")
+    say(f"decode_b32 paged: {kp.shape[0]} blocks of 16, lens sum {lens.sum()}")
     o, lse = _run(q, kp, vp, table, lens, w.scale)
     ro, rl = oa.decode_paged(q, kp, vp, table, lens, block_size=16, scale=w.scale, dtype="bf16")
-    _check_rows(o, lse, ro, rl, "paged c4")
+    _check_rows(o, lse, ro, rl, "paged decode_b32")

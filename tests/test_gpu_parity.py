@@ -137,22 +137,22 @@ def test_deterministic():
 
 
 # ----------------------------------------------------------------- full sizes
-def test_c1_full():
-    w = W.WORKLOADS["c1"]
+def test_f32_n256_full():
+    w = W.WORKLOADS["f32_n256"]
     q, k, v = W.fwd_inputs(w)
-    say("c1: fp32 non-causal B=1 H=1 N=256 d=64")
+    say("f32_n256: fp32 non-causal B=1 H=1 N=256 d=64")
     o, lse = _run_fwd(q, k, v, "f32", False, w.scale, 0.0)
     ro, rl = oa.attention(q, k, v, causal=False, scale=w.scale, dtype="f32")
-    check(o, lse, ro, rl, "f32", "c1 all outputs")
+    check(o, lse, ro, rl, "f32", "f32_n256 all outputs")
 
 
-def test_c2_full():
-    w = W.WORKLOADS["c2"]
+def test_mha_d64_n2048_full():
+    w = W.WORKLOADS["mha_d64_n2048"]
     q, k, v = W.fwd_inputs(w)
-    say("c2: bf16 causal MHA B=4 H=16 N=2048 d=64")
+    say("mha_d64_n2048: bf16 causal MHA B=4 H=16 N=2048 d=64")
     o, lse = _run_fwd(q, k, v, "bf16", True, w.scale, 0.0)
     ro, rl = oa.attention(q, k, v, causal=True, scale=w.scale, dtype="bf16")
-    check(o, lse, ro, rl, "bf16", "c2 all outputs")
+    check(o, lse, ro, rl, "bf16", "mha_d64_n2048 all outputs")
 
 
 def _sampled(w, heads, n_random, seed):
@@ -172,27 +172,27 @@ def _sampled(w, heads, n_random, seed):
         check(o[b, h, rows], lse[b, h, rows], ro, rl, w.dtype, f"{w.name} b={b} h={h} ({len(rows)} rows)")
 
 
-def test_c3_full_size_sampled():
-    w = W.WORKLOADS["c3"]
+def test_gqa_rope_n8192_sampled():
+    w = W.WORKLOADS["gqa_rope_n8192"]
     _sampled(w, [(0, 0), (0, 3), (0, 4), (1, 17), (1, 31)], 48, 3)
 
 
-def test_c5_full_size_sampled():
-    w = W.WORKLOADS["c5"]
+def test_gqa_rope_n32768_sampled():
+    w = W.WORKLOADS["gqa_rope_n32768"]
     _sampled(w, [(0, 0), (0, 7), (0, 8), (0, 63)], 48, 5)
 
 
-def test_c4_full():
+def test_decode_b32_full():
     import torch
-    w = W.WORKLOADS["c4"]
+    w = W.WORKLOADS["decode_b32"]
     lens = W.decode_lens(w)
     q, kc, vc = W.decode_inputs(w, lens)
-    say(f"c4: {w.note}; lens min {lens.min()} max {lens.max()} sum {lens.sum()}")
+    say(f"decode_b32: {w.note}; lens min {lens.min()} max {lens.max()} sum {lens.sum()}")
     o, lse = esd.decode(dev(q), dev(kc), dev(vc), dev(lens), scale=w.scale)
     torch.cuda.synchronize()
     o, lse = host(o), host(lse)
     ro, rl = oa.decode(q, kc, vc, lens, scale=w.scale)
-    check(o, lse, ro, rl, "bf16", "c4 all outputs")
+    check(o, lse, ro, rl, "bf16", "decode_b32 all outputs")
 
 
 # ----------------------------------------------------------------- decode edges
@@ -202,7 +202,7 @@ def test_decode_shapes(Hq, Hkv, d):
     """Lengths 0, 1, batch / wave / chunk edges (32, 128, 1024 keys), several
     chunks, and a NaN-poisoned tail past each length."""
     import torch
-    w = W.WORKLOADS["c4"]
+    w = W.WORKLOADS["decode_b32"]
     lens = np.array([0, 1, 31, 33, 127, 129, 1023, 1024, 1025, 2100, 3000], dtype=np.int32)
     q, kc, vc = W.decode_inputs(w, lens, Hq=Hq, Hkv=Hkv, max_len=3000, d=d, seed_base=7600 + Hq)
     o, lse = esd.decode(dev(q), dev(kc), dev(vc), dev(lens), scale=1 / math.sqrt(d))
@@ -242,7 +242,7 @@ def test_decode_more_chunks_than_merge_slots():
     """A 1.2M-key sequence: 1172 partial states of 1024 keys, more than the 1024
     weights the merge kernel keeps in LDS, so the rest are recomputed."""
     import torch
-    w = W.WORKLOADS["c4"]
+    w = W.WORKLOADS["decode_b32"]
     lens = np.array([1_200_000, 5], dtype=np.int32)
     q, kc, vc = W.decode_inputs(w, lens, Hq=4, Hkv=1, max_len=1_200_000, d=64, seed_base=7900)
     say("decode: one sequence of 1.2M keys (1172 chunks)")

@@ -138,8 +138,8 @@ def _sampled_window(name, w, heads, n_random, seed):
 
 
 def test_window_gqa_n8192_sampled():
-    _sampled_window("c3", 4096, [(0, 0), (0, 5), (1, 31)], 40, 11)
+    _sampled_window("gqa_rope_n8192", 4096, [(0, 0), (0, 5), (1, 31)], 40, 11)
 
 
 def test_window_long_context_n32768_sampled():
-    _sampled_window("c5", 4096, [(0, 0), (0, 9), (0, 63)], 40, 12)
+    _sampled_window("gqa_rope_n32768", 4096, [(0, 0), (0, 9), (0, 63)], 40, 12)

@@ -9,17 +9,18 @@ Workloads (shapes follow the pages' own examples: n = 8192 with d = 128 and
 32 query / 8 KV heads as in Llama-3-8B, 64 query / 8 KV heads as in
 LLaMA-3-70B, a decode batch of 32 sequences):
 
-* ``c1`` single-head non-causal fp32, B=1 H=1 N=256 d=64
-* ``c2`` MHA causal prefill bf16, B=4 H=16 N=2048 d=64
-* ``c3`` GQA causal prefill bf16 with RoPE base 10000, B=2 Hq=32 Hkv=8 N=8192 d=128
-* ``c4`` GQA decode bf16, B=32 Hq=32 Hkv=8 d=128, KV lengths ~ U[1024, 32768]
-* ``c5`` long-context GQA causal prefill bf16 with RoPE base 500000,
+* ``f32_n256`` single-head non-causal fp32, B=1 H=1 N=256 d=64
+* ``mha_d64_n2048`` MHA causal prefill bf16, B=4 H=16 N=2048 d=64
+* ``gqa_rope_n8192`` GQA causal prefill bf16 with RoPE base 10000, B=2 Hq=32 Hkv=8 N=8192 d=128
+* ``decode_b32`` GQA decode bf16, B=32 Hq=32 Hkv=8 d=128, KV lengths ~ U[1024, 32768]
+* ``gqa_rope_n32768`` long-context GQA causal prefill bf16 with RoPE base 500000,
   B=1 Hq=64 Hkv=8 N=32768 d=128, Q and K ~ N(0, 4^2)
 
 Recipe: ``numpy.random.default_rng(seed).standard_normal(shape, float32) * sigma``,
 rounded to bf16 with round-to-nearest-even (fp32 workloads stay fp32).
-Seeds are ``1000*cfg + t`` with t = 1, 2, 3 for Q, K, V; decode lengths come
-from ``default_rng(4004).integers(1024, 32768, size=32, endpoint=True)``.
+Seeds are ``seed_base + t`` with t = 1, 2, 3 for Q, K, V (seed_base 1000, 2000,
+3000, 4000 and 5000 in the order listed); decode lengths come from
+``default_rng(4004).integers(1024, 32768, size=32, endpoint=True)``.
 """
 
 from __future__ import annotations
@@ -61,19 +62,19 @@ class Workload:
 
 
 WORKLOADS = {
-    "c1": Workload("c1", "fwd", B=1, Hq=1, Hkv=1, d=64, dtype="f32", Nq=256, Nk=256,
+    "f32_n256": Workload("f32_n256", "fwd", B=1, Hq=1, Hkv=1, d=64, dtype="f32", Nq=256, Nk=256,
                    causal=False, seed_base=1000,
                    note="single-head non-causal fp32, N=256, d=64"),
-    "c2": Workload("c2", "fwd", B=4, Hq=16, Hkv=16, d=64, dtype="bf16", Nq=2048, Nk=2048,
+    "mha_d64_n2048": Workload("mha_d64_n2048", "fwd", B=4, Hq=16, Hkv=16, d=64, dtype="bf16", Nq=2048, Nk=2048,
                    causal=True, seed_base=2000,
                    note="MHA causal prefill, B=4, H=16, N=2048, d=64"),
-    "c3": Workload("c3", "fwd", B=2, Hq=32, Hkv=8, d=128, dtype="bf16", Nq=8192, Nk=8192,
+    "gqa_rope_n8192": Workload("gqa_rope_n8192", "fwd", B=2, Hq=32, Hkv=8, d=128, dtype="bf16", Nq=8192, Nk=8192,
                    causal=True, rope_base=10000.0, seed_base=3000,
                    note="GQA causal prefill + RoPE 1e4, B=2, Hq=32, Hkv=8, N=8192, d=128"),
-    "c4": Workload("c4", "decode", B=32, Hq=32, Hkv=8, d=128, dtype="bf16",
+    "decode_b32": Workload("decode_b32", "decode", B=32, Hq=32, Hkv=8, d=128, dtype="bf16",
                    max_len=32768, len_lo=1024, len_hi=32768, lens_seed=4004, seed_base=4000,
                    note="GQA decode, B=32, Hq=32, Hkv=8, d=128, lens ~ U[1024, 32768]"),
-    "c5": Workload("c5", "fwd", B=1, Hq=64, Hkv=8, d=128, dtype="bf16", Nq=32768, Nk=32768,
+    "gqa_rope_n32768": Workload("gqa_rope_n32768", "fwd", B=1, Hq=64, Hkv=8, d=128, dtype="bf16", Nq=32768, Nk=32768,
                    causal=True, rope_base=500000.0, sigma_qk=4.0, seed_base=5000,
                    note="long-context GQA causal prefill + RoPE 5e5, B=1, Hq=64, Hkv=8, "
                         "N=32768, d=128, Q,K ~ N(0,16)"),
