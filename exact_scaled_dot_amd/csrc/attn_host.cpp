@@ -143,13 +143,19 @@ int attn_fwd_window(const void* q, const void* k, const void* v, float* o, float
                     workspace, workspace_bytes, stream);
 }
 
-size_t attn_decode_multi_workspace_bytes(int B, int Hq, int Hkv, int T, int max_len, int d) {
+// Partial states of the split decode: one per (row, chunk of `chunk` keys),
+// d floats of O then one float of lse, the two arrays 256-byte aligned.
+static size_t decode_ws_bytes(int B, int Hq, int Hkv, int T, int max_len, int d, int chunk) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0 || max_len <= 0 || d <= 0) return 0;
-    const size_t nch = (size_t)(max_len + attn::kDecodeChunk - 1) / attn::kDecodeChunk;
+    const size_t nch = (size_t)(max_len + chunk - 1) / chunk;
     const size_t rows = (size_t)B * Hq * T * nch;
     size_t o_bytes = rows * d * sizeof(float);
     o_bytes = (o_bytes + 255) & ~(size_t)255;
     return o_bytes + rows * sizeof(float);
+}
+
+size_t attn_decode_multi_workspace_bytes(int B, int Hq, int Hkv, int T, int max_len, int d) {
+    return decode_ws_bytes(B, Hq, Hkv, T, max_len, d, attn::decode_chunk(false));
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int d) {
@@ -161,7 +167,7 @@ size_t attn_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int T, int max_
     if (max_blocks <= 0 || block_size <= 0) return 0;
     const long long max_len = (long long)max_blocks * block_size;
     if (max_len > 0x7fffffffLL) return 0;
-    return attn_decode_multi_workspace_bytes(B, Hq, Hkv, T, (int)max_len, d);
+    return decode_ws_bytes(B, Hq, Hkv, T, (int)max_len, d, attn::decode_chunk(true));
 }
 
 }  // extern "C"
@@ -194,7 +200,8 @@ int decode_impl(const void* q, const void* k, const void* v, const int32_t* tabl
     if (!q || !k || !v || !seq_lens || !o) return fail(ATTN_ERR_INVALID, "null pointer");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return fail(ATTN_ERR_INVALID, "q, caches and o must be 16-byte aligned");
-    const size_t need = attn_decode_multi_workspace_bytes(B, Hq, Hkv, T, max_len, d);
+    const int chunk = attn::decode_chunk(table != nullptr);
+    const size_t need = decode_ws_bytes(B, Hq, Hkv, T, max_len, d, chunk);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(ATTN_ERR_WORKSPACE, "decode workspace missing or too small");
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
@@ -220,7 +227,8 @@ int decode_impl(const void* q, const void* k, const void* v, const int32_t* tabl
         a.rope_tab = attn::rope_table(dev, rope_base, d, max_len, &e);
         if (!a.rope_tab) return fail(ATTN_ERR_HIP, "RoPE table");
     }
-    a.nchunks = (max_len + attn::kDecodeChunk - 1) / attn::kDecodeChunk;
+    a.chunk = chunk;
+    a.nchunks = (max_len + chunk - 1) / chunk;
     const size_t rows = (size_t)B * Hq * T * a.nchunks;
     size_t o_bytes = (rows * d * sizeof(float) + 255) & ~(size_t)255;
     a.ws_o = static_cast<float*>(workspace);

@@ -18,7 +18,7 @@
 //   lse = (M + log2 sum_c w_c) * ln 2.
 //
 // gfx950 mapping of the split kernel (one KV head, up to 16 query columns,
-// 1024 keys: 128 per wave, 8 waves).  A column is one (query head, new token)
+// 2048 keys, 1024 for a paged cache: 256 or 128 per wave, 8 waves).  A column is one (query head, new token)
 // pair; the G*T columns of a KV head are G*T consecutive rows of q, so they
 // are numbered in that order and each keeps its own last visible key:
 //   * each wave streams its K rows and then its V rows in 32-key batches
@@ -38,7 +38,10 @@
 //     the V operand is read with the transposing LDS load ds_read_b64_tr_b16.  O is normalised by the sum of the rounded
 //     weights (v_dot2c_f32_bf16), the log-sum by the fp32 sum.
 //   * the eight waves' partial states are merged in LDS with the same rule the
-//     merge kernel uses, giving one partial state per 1024-key chunk.
+//     merge kernel uses, giving one partial state per chunk.  (At 1024 keys
+//     per chunk the fp32 partial states of a 4-token decode cost 5% of the
+//     cache bytes; at 2048 half that, and one-token decode is unchanged.  The
+//     paged kernel keeps 1024: at 2048 its per-block load resources spill.)
 //   * paged cache ("Attention mechanisms: from alignment to efficient long
 //     context", section 20; "Transformer Architecture Breakdown", Paged
 //     Attention): the pools are [num_blocks, Hkv, block_size, d] and token p of
@@ -61,11 +64,8 @@ namespace {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kCh = kDecodeChunk;       // keys per workgroup
 constexpr int kSplitWaves = 8;          // waves per split workgroup
-constexpr int kWaveKeys = kCh / kSplitWaves;  // keys per wave
 constexpr int kBatch = 32;              // keys per streamed batch
-constexpr int kNB = kWaveKeys / kBatch; // batches per wave
 
 __device__ __forceinline__ float sum_bf16x2(uint32_t two, float acc) {
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -93,6 +93,10 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     int max_blocks, int lbs, int num_blocks) {
     static_assert(D == 64 || D == 128, "head dim");
     static_assert(GP >= 1 && GP <= 16, "columns per workgroup");
+    constexpr int kCh = decode_chunk(PAGED);          // keys per workgroup
+    constexpr int kWaveKeys = kCh / kSplitWaves;      // keys per wave
+    constexpr int kNB = kWaveKeys / kBatch;           // batches per wave
+    static_assert(kWaveKeys <= 64 * 16, "a wave's table entries fit its lanes (blocks >= 16)");
     constexpr int NS = D / 32;          // QK MFMA k-steps over d
     constexpr int NDB = D / 16;         // PV output blocks of 16 dims
     constexpr int VSD = D + 16;         // V row stride in LDS: 8 banks mod 64
@@ -371,7 +375,8 @@ template <int D>
 __global__ void __launch_bounds__(256)
 decode_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
                     const int32_t* __restrict__ lens, float* __restrict__ o,
-                    float* __restrict__ lse, int Hq, int T, int max_len, int nchunks) {
+                    float* __restrict__ lse, int Hq, int T, int max_len, int nchunks,
+                    int kCh) {
     constexpr int NSPLIT = 256 / D;
     __shared__ float wts[1024];
     __shared__ float red[8];
@@ -474,7 +479,7 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     const long long rows = (long long)a.B * a.Hq * a.T;
     if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     decode_merge_kernel<D><<<(unsigned)rows, 256, 0, stream>>>(
-        a.ws_o, a.ws_lse, a.lens, a.o, a.lse, a.Hq, a.T, a.max_len, a.nchunks);
+        a.ws_o, a.ws_lse, a.lens, a.o, a.lse, a.Hq, a.T, a.max_len, a.nchunks, a.chunk);
     return hipGetLastError();
 }
 

@@ -47,9 +47,15 @@ struct DecodeArgs {
     float* ws_o;    // [B, Hq, T, nchunks, d]
     float* ws_lse;  // [B, Hq, T, nchunks] (log2 domain)
     int nchunks;
+    int chunk;      // keys per split workgroup (decode_chunk(paged))
 };
 
-constexpr int kDecodeChunk = 1024;  // keys per split workgroup
+// Keys per split workgroup: 2048 for a contiguous cache (half the partial
+// states of 1024, which matters once several new tokens share a chunk); 1024
+// for a paged cache, whose per-block load resources need the registers.
+constexpr int kDecodeChunk = 2048;
+constexpr int kDecodeChunkPaged = 1024;
+constexpr int decode_chunk(bool paged) { return paged ? kDecodeChunkPaged : kDecodeChunk; }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 

@@ -172,7 +172,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 attn_dtype dtype, void* workspace, size_t workspace_bytes,
                 hipStream_t stream);
 
-/* Bytes of workspace attn_decode_multi needs: B*Hq*T*ceil(max_len/1024)
+/* Bytes of workspace attn_decode_multi needs: B*Hq*T*ceil(max_len/2048)
  * partial states of d + 1 floats (256-byte aligned split). */
 size_t attn_decode_multi_workspace_bytes(int B, int Hq, int Hkv, int T, int max_len, int d);
 
@@ -206,8 +206,10 @@ int attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
                       float rope_base, attn_dtype dtype, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of workspace attn_decode_paged needs: as attn_decode_multi with
- * max_len = max_blocks * block_size (0 when that overflows). */
+/* Bytes of workspace attn_decode_paged needs: B*Hq*T*ceil(max_len/1024)
+ * partial states of d + 1 floats with max_len = max_blocks * block_size (the
+ * paged kernel splits the cache into chunks of 1024 keys); 0 when that
+ * product overflows. */
 size_t attn_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int T, int max_blocks,
                                          int block_size, int d);
 

@@ -40,7 +40,7 @@ def test_workspace_sizes():
     assert esd.fwd_workspace_bytes(2, 8, 8192, 128, 10000.0, esd.ATTN_BF16) == 2 * 8 * 8192 * 128 * 2
     assert esd.fwd_workspace_bytes(1, 1, 256, 64, 100.0, esd.ATTN_F32) == 256 * 64 * 4
     n = esd.decode_workspace_bytes(32, 32, 8, 32768, 128)
-    rows = 32 * 32 * (32768 // 1024)  # one partial state per 1024-key chunk
+    rows = 32 * 32 * (32768 // 2048)  # one partial state per 2048-key chunk
     assert n >= rows * 129 * 4 and n < rows * 129 * 4 + 256
     assert esd.decode_workspace_bytes(0, 32, 8, 32768, 128) == 0
 
@@ -142,7 +142,7 @@ def test_decode_multi_rejects_on_host(kw, code):
 def test_decode_multi_workspace():
     one = esd.decode_workspace_bytes(3, 8, 2, 5000, 128)
     assert esd.decode_multi_workspace_bytes(3, 8, 2, 1, 5000, 128) == one
-    rows = 3 * 8 * 6 * 5  # B * Hq * T * chunks of 1024 keys
+    rows = 3 * 8 * 6 * 3  # B * Hq * T * chunks of 2048 keys
     n = esd.decode_multi_workspace_bytes(3, 8, 2, 6, 5000, 128)
     assert rows * 129 * 4 <= n < rows * 129 * 4 + 256
     assert esd.decode_multi_workspace_bytes(3, 8, 2, 0, 5000, 128) == 0
@@ -170,6 +170,13 @@ def test_decode_paged_rejects_on_host(kw, code):
 def test_decode_paged_workspace_and_noop():
     assert (esd.decode_paged_workspace_bytes(3, 8, 2, 2, 20, 16, 128)
             == esd.decode_multi_workspace_bytes(3, 8, 2, 2, 320, 128))
+    # 3200 keys: a paged cache is split into chunks of 1024 keys (4 partial
+    # states per row), a contiguous one into chunks of 2048 (2 per row)
+    rows_paged, rows_contig = 3 * 8 * 2 * 4, 3 * 8 * 2 * 2
+    n = esd.decode_paged_workspace_bytes(3, 8, 2, 2, 200, 16, 128)
+    assert rows_paged * 129 * 4 <= n < rows_paged * 129 * 4 + 256
+    n = esd.decode_multi_workspace_bytes(3, 8, 2, 2, 3200, 128)
+    assert rows_contig * 129 * 4 <= n < rows_contig * 129 * 4 + 256
     assert esd.decode_paged_workspace_bytes(3, 8, 2, 2, 1 << 20, 1 << 12, 128) == 0
     assert _decp(B=0, q=None, k=None, v=None, table=None, lens=None, o=None, ws=None, wsb=0) == 0
 

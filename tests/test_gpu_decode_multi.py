@@ -23,7 +23,8 @@ pytestmark = pytest.mark.gpu
 
 esd = pytest.importorskip("exact_scaled_dot_amd")
 
-LENS = np.array([0, 1, 2, 3, 5, 31, 33, 127, 1023, 1024, 1025, 1027, 2100, 3000], dtype=np.int32)
+LENS = np.array([0, 1, 2, 3, 5, 31, 33, 127, 1023, 1024, 1025, 1027, 2047, 2048, 2049, 2100, 3000,
+                 4097], dtype=np.int32)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -61,7 +62,7 @@ def _check_rows(o, lse, ro, rl, what):
                                       (32, 1, 2), (12, 4, 7), (8, 2, 16)])
 @pytest.mark.parametrize("d", [64, 128])
 def test_decode_multi_shapes(Hq, Hkv, T, d):
-    q, kc, vc = _inputs(LENS, Hq, Hkv, T, 3000, d, 9000 + 10 * Hq + T)
+    q, kc, vc = _inputs(LENS, Hq, Hkv, T, 4100, d, 9000 + 10 * Hq + T)
     o, lse = _run(q, kc, vc, LENS, 1 / math.sqrt(d))
     ro, rl = oa.decode_multi(q, kc, vc, LENS, scale=1 / math.sqrt(d), dtype="bf16")
     _check_rows(o, lse, ro, rl, f"decode_multi Hq={Hq} Hkv={Hkv} T={T} d={d}")
@@ -69,7 +70,7 @@ def test_decode_multi_shapes(Hq, Hkv, T, d):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_decode_multi_rope(d):
-    q, kc, vc = _inputs(LENS, 16, 4, 4, 3000, d, 9400 + d)
+    q, kc, vc = _inputs(LENS, 16, 4, 4, 4100, d, 9400 + d)
     o, lse = _run(q, kc, vc, LENS, 1 / math.sqrt(d), rope_base=10000.0)
     ro, rl = oa.decode_multi(q, kc, vc, LENS, scale=1 / math.sqrt(d), rope_base=10000.0, dtype="bf16")
     _check_rows(o, lse, ro, rl, f"decode_multi rope d={d}")
@@ -77,7 +78,7 @@ def test_decode_multi_rope(d):
 
 def test_decode_multi_t1_equals_decode():
     import torch
-    q, kc, vc = _inputs(LENS, 32, 8, 1, 3000, 128, 9500)
+    q, kc, vc = _inputs(LENS, 32, 8, 1, 4100, 128, 9500)
     a = _run(q, kc, vc, LENS, 0.0884)
     o, lse = esd.decode(dev(q[:, :, 0]), dev(kc), dev(vc), dev(LENS), scale=0.0884)
     torch.cuda.synchronize()

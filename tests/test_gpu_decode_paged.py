@@ -5,9 +5,12 @@ p % block_size ("Attention mechanisms: from alignment to efficient long
 context", section 20).  The pools hold NaN in every row no sequence owns (spare
 blocks, the tail of each last block) and the tables hold -1 past each
 sequence's blocks, so a read of anything outside the sequence would show.
-Tolerances as for contiguous decode (bf16: max|dO| <= 1e-2, max|dlse| <= 1e-3);
-paged and contiguous decode of the same rows must agree bit for bit, since the
-arithmetic and its order are the same.
+Tolerances as for contiguous decode (bf16: max|dO| <= 1e-2, max|dlse| <= 1e-3).
+Paged and contiguous decode of the same rows are compared with each other too.
+They split the cache into chunks of 1024 and 2048 keys, so each wave's reference
+max, and with it the bf16 rounding of the weights, differs. The two therefore
+agree to max|dO| <= 1e-3 (bf16 weight rounding) and max|dlse| <= 2e-5 (fp32 sums).
+A key row read from the wrong place moves lse by about 1 / length, far more.
 """
 
 import math
@@ -23,7 +26,8 @@ pytestmark = pytest.mark.gpu
 
 esd = pytest.importorskip("exact_scaled_dot_amd")
 
-LENS = np.array([0, 1, 2, 15, 16, 17, 31, 33, 127, 1023, 1024, 1025, 1040, 2100, 3000],
+LENS = np.array([0, 1, 2, 15, 16, 17, 31, 33, 127, 1023, 1024, 1025, 1040, 2047, 2048, 2049, 2100,
+                 3000, 4112],
                 dtype=np.int32)
 
 
@@ -67,7 +71,8 @@ def test_decode_paged_shapes(bs, Hq, Hkv, T, d):
 
 @pytest.mark.parametrize("bs", [16, 128])
 def test_decode_paged_equals_contiguous(bs):
-    """The same rows laid out contiguously give identical outputs."""
+    """The same rows laid out contiguously give the same outputs (to the rounding
+    of the bf16 weights; lse to fp32 rounding)."""
     import torch
     w = W.WORKLOADS["decode_b32"]
     q, kp, vp, table = W.paged_inputs(w, LENS, block_size=bs, T=3, Hq=32, Hkv=8, d=128,
@@ -82,7 +87,14 @@ def test_decode_paged_equals_contiguous(bs):
         vc[b, :, :n] = vp[table[b, pos // bs], :, pos % bs].transpose(1, 0, 2)
     oc, lc = esd.decode_multi(dev(q), dev(kc), dev(vc), dev(LENS), scale=0.0884, rope_base=10000.0)
     torch.cuda.synchronize()
-    assert np.array_equal(o, host(oc)) and np.array_equal(lse, host(lc))
+    oc, lc = host(oc), host(lc)
+    dead = np.isneginf(lc)
+    assert np.array_equal(np.isneginf(lse), dead)
+    assert np.all(o[dead] == 0) and np.all(oc[dead] == 0)
+    do = float(np.max(np.abs(o[~dead].astype(np.float64) - oc[~dead])))
+    dl = float(np.max(np.abs(lse[~dead].astype(np.float64) - lc[~dead])))
+    say(f"paged bs={bs} vs contiguous: max|dO| = {do:.3e} (tol 1e-3), max|dlse| = {dl:.3e} (tol 2e-5)")
+    assert do <= 1e-3 and dl <= 2e-5
 
 
 def test_decode_paged_rope():

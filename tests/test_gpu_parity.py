@@ -199,12 +199,13 @@ def test_decode_b32_full():
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (32, 8), (16, 2), (32, 1), (12, 4), (64, 2)])
 @pytest.mark.parametrize("d", [64, 128])
 def test_decode_shapes(Hq, Hkv, d):
-    """Lengths 0, 1, batch / wave / chunk edges (32, 128, 1024 keys), several
+    """Lengths 0, 1, batch / wave / chunk edges (32, 256, 2048 keys), several
     chunks, and a NaN-poisoned tail past each length."""
     import torch
     w = W.WORKLOADS["decode_b32"]
-    lens = np.array([0, 1, 31, 33, 127, 129, 1023, 1024, 1025, 2100, 3000], dtype=np.int32)
-    q, kc, vc = W.decode_inputs(w, lens, Hq=Hq, Hkv=Hkv, max_len=3000, d=d, seed_base=7600 + Hq)
+    lens = np.array([0, 1, 31, 33, 127, 129, 1023, 1024, 1025, 2047, 2048, 2049, 3000, 4097],
+                    dtype=np.int32)
+    q, kc, vc = W.decode_inputs(w, lens, Hq=Hq, Hkv=Hkv, max_len=4100, d=d, seed_base=7600 + Hq)
     o, lse = esd.decode(dev(q), dev(kc), dev(vc), dev(lens), scale=1 / math.sqrt(d))
     torch.cuda.synchronize()
     o, lse = host(o), host(lse)
@@ -239,14 +240,14 @@ def test_fwd_errors_raise():
 
 
 def test_decode_more_chunks_than_merge_slots():
-    """A 1.2M-key sequence: 1172 partial states of 1024 keys, more than the 1024
+    """A 2.2M-key sequence: 1075 partial states of 2048 keys, more than the 1024
     weights the merge kernel keeps in LDS, so the rest are recomputed."""
     import torch
     w = W.WORKLOADS["decode_b32"]
-    lens = np.array([1_200_000, 5], dtype=np.int32)
-    q, kc, vc = W.decode_inputs(w, lens, Hq=4, Hkv=1, max_len=1_200_000, d=64, seed_base=7900)
-    say("decode: one sequence of 1.2M keys (1172 chunks)")
+    lens = np.array([2_200_000, 5], dtype=np.int32)
+    q, kc, vc = W.decode_inputs(w, lens, Hq=4, Hkv=1, max_len=2_200_000, d=64, seed_base=7900)
+    say("decode: one sequence of 2.2M keys (1075 chunks)")
     o, lse = esd.decode(dev(q), dev(kc), dev(vc), dev(lens), scale=0.125)
     torch.cuda.synchronize()
     ro, rl = oa.decode(q, kc, vc, lens, scale=0.125)
-    check(host(o), host(lse), ro, rl, "bf16", "decode 1.2M keys")
+    check(host(o), host(lse), ro, rl, "bf16", "decode 2.2M keys")
