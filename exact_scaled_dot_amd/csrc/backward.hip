@@ -20,12 +20,12 @@
 //     wave: S = Q K^T and dP = dO V^T (row-read A operands), then
 //     dV += P^T dO and dK += dS^T Q with P and dS straight from the score
 //     registers as A operands and dO, Q read with the transposing LDS load.
-//   * dQ: laid out like the forward (8 waves, 32 query rows each, GQA heads
-//     sharing K/V tiles of 64 keys): S^T = K Q^T and dP^T = V dO^T, then
-//     dQ^T += K^T dS^T with K read transposed.
-// Both stream their tiles through two LDS buffers: the next tile is loaded
-// into registers while the current one is computed, with one barrier per
-// tile.
+//   * dQ: 8 waves, 32 query rows each, GQA heads sharing K/V tiles of 64
+//     keys: S^T = K Q^T and dP^T = V dO^T, then dQ^T += K^T dS^T with K read
+//     transposed.
+// Both stream their tiles through two LDS buffers with one barrier per tile:
+// the next tile is loaded while the current one is computed (dK/dV straight
+// into LDS, dQ through registers).
 // A tile that is read both by rows (16 bytes per lane, 16 lanes per LDS cycle:
 // the row stride must be an odd multiple of 4 banks) and transposed (four
 // rows' 64-byte pieces per cycle: an odd multiple of 16 banks) is stored

@@ -88,7 +88,6 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     int nchunks, int nrb, int win) {
     static_assert(!WINDOW || CAUSAL, "the sliding window is built for causal attention");
     constexpr int kWaves = waves_for<D>();
-    constexpr int NT = kWaves * 64;
     constexpr int KS = D + kKPad;       // K row stride in LDS (elements)
     constexpr int VS = D + kVPad;       // V row stride in LDS (elements)
     constexpr int CPR = D / 8;          // 16-byte chunks per row
