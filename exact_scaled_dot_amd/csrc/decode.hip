@@ -182,16 +182,22 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         const int bi = e < kNB ? e : e - kNB;
         if constexpr (PAGED) {
             const uint16_t* pool = e < kNB ? k : v;
+            // one resource per 16 keys (the smallest block), shared by the
+            // JPG load instructions that cover them
+            constexpr int JPG = 16 / KPJ;
 #pragma unroll
-            for (int j = 0; j < VPL; ++j) {
-                const int key = wk0 + kBatch * bi + KPJ * j;  // first key of this load
+            for (int gi = 0; gi < VPL / JPG; ++gi) {
+                const int key = wk0 + kBatch * bi + 16 * gi;  // first key of the group
                 const int ks = key & -(1 << lbs);             // first key of its block
                 const int phys = __builtin_amdgcn_readlane(ent, (key >> lbs) - (wk0 >> lbs));
                 const int nvalid = min(max(len - ks, 0), 1 << lbs);
                 const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
                     const_cast<uint16_t*>(pool + ((size_t)phys * Hkv + g) * ((size_t)D << lbs)),
                     (short)0, nvalid * D * 2, 0x00020000);
-                ring[slot][j] = __builtin_amdgcn_raw_buffer_load_b128(r, (key - ks) * D * 2 + lane_off, 0, kStream);
+#pragma unroll
+                for (int jj = 0; jj < JPG; ++jj)
+                    ring[slot][gi * JPG + jj] = __builtin_amdgcn_raw_buffer_load_b128(
+                        r, (key - ks) * D * 2 + JSTEP * jj + lane_off, 0, kStream);
             }
         } else {
             const int boff = (wk0 + kBatch * bi) * D * 2 + lane_off;
