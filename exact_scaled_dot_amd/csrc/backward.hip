@@ -14,10 +14,13 @@
 //   * prep: per query row, dO rounded to bf16 for the matrix cores, D = dO . O
 //     (fp32) from that rounded dO, lse converted to the log2 domain.
 //   * dK/dV: a workgroup owns 256 keys of one KV head (8 waves x 32 keys, K
-//     and V of a wave held in registers as MFMA operands) and streams 32-query
+//     and V of a wave held in registers as MFMA operands) and streams 64-query
 //     tiles of Q and dO of every query head that reads this KV head through
-//     LDS, so the GQA sum over heads happens in the accumulators.  Per tile and
-//     wave: S = Q K^T and dP = dO V^T (row-read A operands), then
+//     LDS, so the GQA sum over heads happens in the accumulators.  Each tile
+//     takes two updates of 32 queries between barriers, so the two waves of a
+//     SIMD drift out of phase within a tile; a wave skips an update whose rows
+//     see none of its keys (causal).  Per update and wave: S = Q K^T and
+//     dP = dO V^T (row-read A operands), then
 //     dV += P^T dO and dK += dS^T Q with P and dS straight from the score
 //     registers as A operands and dO, Q read with the transposing LDS load.
 //   * dQ: 8 waves, 32 query rows each, GQA heads sharing K/V tiles of 64
@@ -98,7 +101,8 @@ bwd_prep_kernel(const float* __restrict__ o, const float* __restrict__ dout,
 // ------------------------------------------------------------------ dK, dV
 constexpr int kKW = 8;        // waves per dK/dV workgroup (two per SIMD)
 constexpr int kKeysW = 32;    // keys per wave
-constexpr int kQT = 32;       // queries per tile
+constexpr int kQT = 64;       // queries per tile (two 32-query updates per barrier)
+constexpr int kQS = 32;       // queries per update
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kKW * 64, 1)
@@ -166,12 +170,11 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
     // The loop runs over (query head of the group, query tile) pairs, from the
     // first tile holding a position >= k0 (causal).  Pair it+1 is loaded into
-    // registers while pair it is computed (S and dP, then P and dS, then dV and
-    // dK) and stored into the other LDS buffer afterwards; the buffer parity is
-    // a constant in the loop unrolled by two, so every LDS address is a
-    // per-lane base plus an immediate; one barrier per pair, no branch in the
-    // body.  Two waves share each SIMD, so one's vector and LDS work overlaps
-    // the other's matrix products.
+    // the other LDS buffer while pair it is computed (per 32-query update: S
+    // and dP, then P and dS, then dV and dK); the buffer parity is a constant
+    // in the loop unrolled by two, so every LDS address is a per-lane base plus
+    // an immediate; one barrier per pair.  Two waves share each SIMD, so one's
+    // vector and LDS work overlaps the other's matrix products.
     const int qstart = CAUSAL ? max(0, k0 - off) / kQT * kQT : 0;
     const int ntq = (Nq - qstart + kQT - 1) / kQT;
     const int niter = G * ntq;
@@ -214,7 +217,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         dma(ro, Or(P), RS, q0);
         dma(rq, Qt(P), TS, q0);
         dma(ro, Ot(P), TS, q0);
-        // every thread fetches the statistics of row tid % 32 (the same value
+        // every thread fetches the statistics of row tid % 64 (the same value
         // for the same slot, so the stores need no branch).  Buffer loads
         // bounded to this head's rows: rows past Nq read 0, and their lse
         // becomes +inf (P = 2^-inf = 0) by an add, not a select of a load
@@ -222,22 +225,22 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             const_cast<float*>(lse2 + qoff), (short)0, Nq * 4, 0x00020000);
         const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<float*>(dvec + qoff), (short)0, Nq * 4, 0x00020000);
-        const int qr = q0 + l32;
+        const int qr = q0 + lane;
         r.l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, qr * 4, 0, 0)) +
               (qr < Nq ? 0.f : INFINITY);
         r.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, qr * 4, 0, 0));
     };
     auto store_stats = [&](int buf, const Pair& r) {
-        Ls[buf][l32] = r.l;
-        Dsh[buf][l32] = r.d;
+        Ls[buf][lane] = r.l;
+        Dsh[buf][lane] = r.d;
     };
     // S = Q K^T and dP = dO V^T of one tile: lane holds key column l32 and
     // query rows 8*(i/4) + 4*half + i%4
-    auto scores = [&](int buf, f32x16& sa, f32x16& pa) {
+    auto scores = [&](int buf, int sub, f32x16& sa, f32x16& pa) {
         sa = f32x16{};
         pa = f32x16{};
-        const uint16_t* Qb = Qr(buf);
-        const uint16_t* Ob = Or(buf);
+        const uint16_t* Qb = Qr(buf) + kQS * RS * sub;
+        const uint16_t* Ob = Or(buf) + kQS * RS * sub;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
             const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&Qb[l32 * RS + 16 * s + 8 * half]);
@@ -248,12 +251,12 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     };
     // P and dS of one tile, then dV += P^T dO and dK += dS^T Q over its 32
     // queries (two k-steps)
-    auto accumulate = [&](int buf, int q0, const f32x16& sa, const f32x16& pa) {
+    auto accumulate = [&](int buf, int sub, int q0, const f32x16& sa, const f32x16& pa) {
         uint32_t pw[2][4], dw[2][4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][8 * j + 4 * half]);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Dsh[buf][8 * j + 4 * half]);
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][kQS * sub + 8 * j + 4 * half]);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Dsh[buf][kQS * sub + 8 * j + 4 * half]);
             float p[4], ds[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -279,9 +282,9 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             const bf16x8 dA = __builtin_bit_cast(bf16x8, d4);
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-                const bf16x8 bo = tr_fragment(Ob, TS, 16 * ks, 32 * db, lane);
+                const bf16x8 bo = tr_fragment(Ob, TS, kQS * sub + 16 * ks, 32 * db, lane);
                 dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pA, bo, dva[db], 0, 0, 0);
-                const bf16x8 bq = tr_fragment(Qb, TS, 16 * ks, 32 * db, lane);
+                const bf16x8 bq = tr_fragment(Qb, TS, kQS * sub + 16 * ks, 32 * db, lane);
                 dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dA, bq, dka[db], 0, 0, 0);
             }
         }
@@ -299,9 +302,16 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         gload(it + 1, P ^ 1, X);
         // keep the loads here, a whole pair ahead of their use
         __builtin_amdgcn_sched_barrier(0);
-        f32x16 sc, pc;
-        scores(P, sc, pc);
-        accumulate(P, tile_q0(it), sc, pc);
+        const int q0 = tile_q0(it);
+#pragma unroll
+        for (int u = 0; u < kQT / kQS; ++u) {
+            // skip an update none of whose rows sees a key of this wave
+            if (!CAUSAL || q0 + kQS * u + kQS - 1 >= kw0 - off) {
+                f32x16 sc, pc;
+                scores(P, u, sc, pc);
+                accumulate(P, u, q0 + kQS * u, sc, pc);
+            }
+        }
         store_stats(P ^ 1, X);
         dma_wait();
         __syncthreads();
