@@ -93,6 +93,20 @@ def test_bwd_head_sharing(Hq, Hkv):
         _grad_check(a, r, f"bwd {name} Hq={Hq} Hkv={Hkv}")
 
 
+@pytest.mark.parametrize("d,Nq,Nk", [(128, 777, 777), (64, 777, 777), (128, 500, 1100),
+                                     (64, 300, 1030)])
+def test_bwd_causal_several_key_blocks(d, Nq, Nk):
+    """Causal shapes with several 256-key blocks and 64-query tiles, where the
+    waves of a key block skip the 32-query updates none of their keys is
+    visible to at different points (bottom-right offset Nk - Nq included)."""
+    q, k, v, do = _inputs(11600 + Nq + d, 1, 8, 2, Nq, Nk, d)
+    scale = 1 / math.sqrt(d)
+    got = _run(q, k, v, do, True, scale)
+    ref = oa.attention_bwd(q, k, v, do, causal=True, scale=scale, dtype="bf16")
+    for name, a, r in zip(("dq", "dk", "dv"), got, ref):
+        _grad_check(a, r, f"bwd {name} d={d} Nq={Nq} Nk={Nk} causal")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_bwd_rope(d):
     q, k, v, do = _inputs(11300 + d, 2, 8, 2, 150, 200, d)
