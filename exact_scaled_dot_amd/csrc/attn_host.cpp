@@ -357,15 +357,11 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* o, const 
         a.q = qr;
         a.k = kr;
     }
+    // the kernels take the gradients with respect to the rotated rows back to
+    // the rows before rotation as they store them
+    a.rope_t = tab;
     e = attn::launch_bwd_bf16(a, stream);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, hipGetErrorString(e));
-    if (rope_base > 0.f) {
-        // gradients with respect to the rotated rows -> the rows before rotation
-        e = attn::launch_rope_f32_transpose(dq, dq, (long long)rows, Nq, d, Nk - Nq, tab, stream);
-        if (e == hipSuccess)
-            e = attn::launch_rope_f32_transpose(dk, dk, (long long)B * Hkv * Nk, Nk, d, 0, tab, stream);
-        if (e != hipSuccess) return fail(ATTN_ERR_HIP, hipGetErrorString(e));
-    }
     return ATTN_OK;
 }
 

@@ -110,7 +110,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const uint16_t* __restrict__ v, const uint16_t* __restrict__ do16,
                 const float* __restrict__ lse2, const float* __restrict__ dvec,
                 float* __restrict__ dk, float* __restrict__ dv, int B, int Hq, int Hkv, int Nq,
-                int Nk, float scale_log2, float scale) {
+                int Nk, float scale_log2, float scale, const double2* __restrict__ tab) {
     constexpr int NT = kKW * 64;
     constexpr int CPR = D / 8;               // 16-byte chunks per row
     constexpr int NCH = kQT * CPR;           // chunks per tile (of Q and of dO)
@@ -323,16 +323,28 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
     if (it < niter) step(it, 0);
 
-    // lane holds d column 32*db + l32 of key rows kw0 + 8*(i/4) + 4*half + i%4
+    // lane holds d column 32*db + l32 of key rows kw0 + 8*(i/4) + 4*half + i%4.
+    // With RoPE, dK is rotated back here: the pair (2j, 2j+1) of a row sits in
+    // lanes l and l ^ 1, which swap values; each computes its own element of
+    // the transposed rotation at the key's position.
     float* dkb = dk + kvoff;
     float* dvb = dv + kvoff;
+    const bool odd = l32 & 1;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int kr = kw0 + 8 * (i >> 2) + 4 * half + (i & 3);
+            float g = dka[db][i] * scale;
+            if (tab != nullptr) {  // uniform
+                const float other = __shfl_xor(g, 1);
+                const double2 cs = tab[(size_t)min(kr, Nk - 1) * (D / 2) + ((32 * db + l32) >> 1)];
+                float r0, r1;
+                rope_pair_t_f64(odd ? other : g, odd ? g : other, cs.x, cs.y, r0, r1);
+                g = odd ? r1 : r0;
+            }
             if (kr < Nk) {
-                dkb[(size_t)kr * D + 32 * db + l32] = dka[db][i] * scale;
+                dkb[(size_t)kr * D + 32 * db + l32] = g;
                 dvb[(size_t)kr * D + 32 * db + l32] = dva[db][i];
             }
         }
@@ -351,7 +363,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
               const uint16_t* __restrict__ v, const uint16_t* __restrict__ do16,
               const float* __restrict__ lse2, const float* __restrict__ dvec,
               float* __restrict__ dq, int B, int Hq, int Hkv, int Nq, int Nk, float scale_log2,
-              float scale, int hpw, int wph, int nchunks, int nrb) {
+              float scale, int hpw, int wph, int nchunks, int nrb, const double2* __restrict__ tab) {
     constexpr int NT = kQW * 64;
     constexpr int VS = D + kVS;
     constexpr int CPR = D / 8;
@@ -499,16 +511,23 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
 
     if (!ok) return;
-    // lane holds row qi, d = 32db + 8*i4 + 4*half + 0..3
+    // lane holds row qi, d = 32db + 8*i4 + 4*half + 0..3: two whole pairs, which
+    // with RoPE are rotated back at the query's position
     float* drow_out = dq + qrow * D;
+    const double2* trow = tab != nullptr ? tab + (size_t)qpos * (D / 2) : nullptr;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
             const int d = 32 * db + 8 * i4 + 4 * half;
-            *reinterpret_cast<float4*>(drow_out + d) =
-                make_float4(acc[db][4 * i4] * scale, acc[db][4 * i4 + 1] * scale,
-                            acc[db][4 * i4 + 2] * scale, acc[db][4 * i4 + 3] * scale);
+            float4 r = make_float4(acc[db][4 * i4] * scale, acc[db][4 * i4 + 1] * scale,
+                                   acc[db][4 * i4 + 2] * scale, acc[db][4 * i4 + 3] * scale);
+            if (trow != nullptr) {  // uniform
+                const double2 t0 = trow[d >> 1], t1 = trow[(d >> 1) + 1];
+                rope_pair_t_f64(r.x, r.y, t0.x, t0.y, r.x, r.y);
+                rope_pair_t_f64(r.z, r.w, t1.x, t1.y, r.z, r.w);
+            }
+            *reinterpret_cast<float4*>(drow_out + d) = r;
         }
     }
 }
@@ -530,11 +549,11 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     if (a.causal)
         bwd_dkdv_kernel<D, true><<<(unsigned)nwg1, kKW * 64, 0, stream>>>(
             a.q, a.k, a.v, a.do16, a.lse2, a.dvec, a.dk, a.dv, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,
-            scale_log2, a.scale);
+            scale_log2, a.scale, a.rope_t);
     else
         bwd_dkdv_kernel<D, false><<<(unsigned)nwg1, kKW * 64, 0, stream>>>(
             a.q, a.k, a.v, a.do16, a.lse2, a.dvec, a.dk, a.dv, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,
-            scale_log2, a.scale);
+            scale_log2, a.scale, a.rope_t);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
@@ -548,11 +567,11 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     if (a.causal)
         bwd_dq_kernel<D, true><<<(unsigned)nwg2, kQW * 64, 0, stream>>>(
             a.q, a.k, a.v, a.do16, a.lse2, a.dvec, a.dq, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,
-            scale_log2, a.scale, hpw, wph, nchunks, nrb);
+            scale_log2, a.scale, hpw, wph, nchunks, nrb, a.rope_t);
     else
         bwd_dq_kernel<D, false><<<(unsigned)nwg2, kQW * 64, 0, stream>>>(
             a.q, a.k, a.v, a.do16, a.lse2, a.dvec, a.dq, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,
-            scale_log2, a.scale, hpw, wph, nchunks, nrb);
+            scale_log2, a.scale, hpw, wph, nchunks, nrb, a.rope_t);
     return hipGetLastError();
 }
 

@@ -75,14 +75,13 @@ struct BwdArgs {
     uint16_t* do16;  // workspace: dO in bf16 [B, Hq, Nq, d]
     float* dvec;     // workspace: rowsum(dO * O) [B, Hq, Nq]
     float* lse2;     // workspace: lse * log2(e) [B, Hq, Nq]
+    // RoPE table (null: no RoPE).  The kernels store dQ and dK rotated back
+    // (the transpose of the rotation, fp64, rounded to fp32) at their rows'
+    // positions: queries at Nk - Nq + i, keys at j.
+    const double2* rope_t;
 };
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
-
-// out[bh, n, :] = rotate(x[bh, n, :], -(pos_offset + n)) in fp64, rounded to fp32:
-// the transpose of the RoPE rotation, for gradients.
-hipError_t launch_rope_f32_transpose(const float* x, float* out, long long rows, int N, int d,
-                                     int pos_offset, const double2* tab, hipStream_t stream);
 
 // Device table of (cos, sin) in fp64, [npos][d/2]; created or grown on demand.
 // Returns null on failure (HIP error stored in *err).

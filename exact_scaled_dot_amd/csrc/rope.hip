@@ -94,26 +94,6 @@ rope_f32_kernel(const float* __restrict__ x, float* __restrict__ out, long long 
     }
 }
 
-// One thread rotates 4 fp32 (2 pairs) of a row by the negative angle.
-__global__ void __launch_bounds__(256)
-rope_f32_t_kernel(const float* __restrict__ x, float* __restrict__ out, long long nvec, int N,
-                  int d, int pos_offset, const double2* __restrict__ tab) {
-    const int vec_per_row = d >> 2;
-    const int half = d >> 1;
-    for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < nvec;
-         i += (long long)gridDim.x * blockDim.x) {
-        const long long row = i / vec_per_row;
-        const int d0 = (int)(i - row * vec_per_row) << 2;
-        const int pos = pos_offset + (int)(row % N);
-        const double2* t = tab + (size_t)pos * half + (d0 >> 1);
-        const float4 v = *reinterpret_cast<const float4*>(x + row * d + d0);
-        float4 r;
-        rope_pair_t_f64(v.x, v.y, t[0].x, t[0].y, r.x, r.y);
-        rope_pair_t_f64(v.z, v.w, t[1].x, t[1].y, r.z, r.w);
-        *reinterpret_cast<float4*>(out + row * d + d0) = r;
-    }
-}
-
 static int grid_for(long long nvec) {
     long long g = (nvec + 255) / 256;
     if (g > 256 * 64) g = 256 * 64;  // grid-stride beyond 64 workgroups per CU
@@ -133,14 +113,6 @@ hipError_t launch_rope_f32(const float* x, float* out, long long rows, int N, in
     const long long nvec = rows * (d / 4);
     if (nvec == 0) return hipSuccess;
     rope_f32_kernel<<<grid_for(nvec), 256, 0, stream>>>(x, out, nvec, N, d, pos_offset, tab);
-    return hipGetLastError();
-}
-
-hipError_t launch_rope_f32_transpose(const float* x, float* out, long long rows, int N, int d,
-                                     int pos_offset, const double2* tab, hipStream_t stream) {
-    const long long nvec = rows * (d / 4);
-    if (nvec == 0) return hipSuccess;
-    rope_f32_t_kernel<<<grid_for(nvec), 256, 0, stream>>>(x, out, nvec, N, d, pos_offset, tab);
     return hipGetLastError();
 }
 
