@@ -25,7 +25,7 @@
 //     registers as A operands and dO, Q read with the transposing LDS load.
 //   * dQ: 8 waves, 32 query rows each, GQA heads sharing K/V tiles of 64
 //     keys: S^T = K Q^T and dP^T = V dO^T, then dQ^T += K^T dS^T with K read
-//     transposed.
+//     transposed; a wave skips the 32-key halves past its last row (causal).
 // Both stream their tiles through two LDS buffers with one barrier per tile:
 // the next tile is loaded while the current one is computed (dK/dV straight
 // into LDS, dQ through registers).
@@ -401,6 +401,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int off = Nk - Nq;
     const int qpos = off + qi;
     const int klast = CAUSAL ? min(Nk - 1, qpos) : Nk - 1;  // last key this row sees
+    // last key any row of this wave sees (causal): later 32-key halves are skipped
+    const int wave_klast = off + min(Nq - 1, row0 + sub * kRows + kRows - 1);
     int kend = Nk;
     if (CAUSAL) kend = min(Nk, off + min(Nq, row0 + wph * kRows));
     const int ntiles = (kend + kBc - 1) / kBc;
@@ -467,6 +469,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const uint16_t* Vt = Vs[buf];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            if (CAUSAL && key0 + 32 * kb > wave_klast) break;  // wave-uniform
             // S^T = K Q^T and dP^T = V dO^T for 32 keys: lane holds query l32,
             // keys key0 + 32kb + 8*(i/4) + 4*half + i%4
             f32x16 sacc = f32x16{}, pacc = f32x16{};
