@@ -21,8 +21,6 @@ size_t elem_size(attn_dtype t) { return t == ATTN_F32 ? 4 : 2; }
 
 bool known_dtype(int t) { return t == ATTN_BF16 || t == ATTN_F32; }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
-
 bool log_enabled() {
     static int on = -1;
     if (on < 0) {

@@ -111,13 +111,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const float* __restrict__ lse2, const float* __restrict__ dvec,
                 float* __restrict__ dk, float* __restrict__ dv, int B, int Hq, int Hkv, int Nq,
                 int Nk, float scale_log2, float scale, const double2* __restrict__ tab) {
-    constexpr int NT = kKW * 64;
-    constexpr int CPR = D / 8;               // 16-byte chunks per row
-    constexpr int NCH = kQT * CPR;           // chunks per tile (of Q and of dO)
-    // chunks per thread; with fewer chunks than threads (d = 64) two threads
-    // copy the same chunk, storing the same value
-    constexpr int LPT = (NCH + NT - 1) / NT;
-    static_assert(NCH % NT == 0 || NT % NCH == 0, "tile/thread mismatch");
+    constexpr int CPR = D / 8;   // 16-byte chunks per row
     constexpr int RS = D + kRP;  // stride of the row-read copies
     constexpr int TS = D + kTP;  // stride of the transposed-read copies
     // Tiles go from memory straight into LDS (buffer_load ... lds, 1 KB per

@@ -55,7 +55,7 @@ const double2* rope_table(int device, float base, int d, int npos, hipError_t* e
     hipError_t e = hipMalloc(&dev, host.size() * sizeof(double2));
     if (e != hipSuccess) { *err = e; return nullptr; }
     e = hipMemcpy(dev, host.data(), host.size() * sizeof(double2), hipMemcpyHostToDevice);
-    if (e != hipSuccess) { *err = e; hipFree(dev); return nullptr; }
+    if (e != hipSuccess) { *err = e; (void)hipFree(dev); return nullptr; }
     t.ptr = dev;
     t.npos = cap;
     return dev;
