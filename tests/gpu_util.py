@@ -1,6 +1,5 @@
 """Helpers for the GPU tests: move seeded numpy inputs to the device and compare."""
 
-import math
 import sys
 
 import numpy as np
