@@ -69,6 +69,26 @@ def test_decode_paged_shapes(bs, Hq, Hkv, T, d):
     _check_rows(o, lse, ro, rl, f"paged bs={bs} Hq={Hq} Hkv={Hkv} T={T} d={d}")
 
 
+LENS_LONG = np.array([0, 1, 1023, 1024, 1025, 2048, 4095, 4096, 4097, 5000, 8192, 9001],
+                     dtype=np.int32)
+
+
+@pytest.mark.parametrize("bs", [512, 1024, 2048, 4096])
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_paged_large_blocks(bs, d):
+    """Blocks as long as a split workgroup's 1024-key chunk, or longer (up to the
+    largest supported size): several chunks read one block, and a block's tail
+    past the sequence length holds NaN that must never be read."""
+    w = W.WORKLOADS["decode_b32"]
+    q, kp, vp, table = W.paged_inputs(w, LENS_LONG, block_size=bs, T=2, Hq=16, Hkv=4, d=d,
+                                      seed_base=9900 + bs + d)
+    scale = 1 / math.sqrt(d)
+    o, lse = _run(q, kp, vp, table, LENS_LONG, scale)
+    ro, rl = oa.decode_paged(q, kp, vp, table, LENS_LONG, block_size=bs, scale=scale,
+                             dtype="bf16")
+    _check_rows(o, lse, ro, rl, f"paged bs={bs} d={d}")
+
+
 @pytest.mark.parametrize("bs", [16, 128])
 def test_decode_paged_equals_contiguous(bs):
     """The same rows laid out contiguously give the same outputs (to the rounding
