@@ -117,6 +117,20 @@ def test_bwd_rope(d):
         _grad_check(a, r, f"bwd rope {name} d={d}")
 
 
+@pytest.mark.parametrize("d,Nq,Nk", [(128, 500, 1100), (64, 700, 700)])
+def test_bwd_rope_several_key_blocks(d, Nq, Nk):
+    """RoPE with several 256-key blocks: dQ and dK are rotated back in the
+    kernels' stores (dK from pairs split over neighbouring lanes), at query
+    positions Nk - Nq + i and key positions j."""
+    q, k, v, do = _inputs(11700 + Nq + d, 1, 8, 2, Nq, Nk, d)
+    scale = 1 / math.sqrt(d)
+    got = _run(q, k, v, do, True, scale, rope_base=10000.0)
+    ref = oa.attention_bwd(q, k, v, do, causal=True, scale=scale, rope_base=10000.0,
+                           dtype="bf16")
+    for name, a, r in zip(("dq", "dk", "dv"), got, ref):
+        _grad_check(a, r, f"bwd rope {name} d={d} Nq={Nq} Nk={Nk}")
+
+
 def test_bwd_deterministic():
     q, k, v, do = _inputs(11400, 1, 8, 2, 257, 257, 128)
     a = _run(q, k, v, do, True, 0.0884, 10000.0)
