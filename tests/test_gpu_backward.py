@@ -131,6 +131,16 @@ def test_bwd_rope_several_key_blocks(d, Nq, Nk):
         _grad_check(a, r, f"bwd rope {name} d={d} Nq={Nq} Nk={Nk}")
 
 
+@pytest.mark.parametrize("d,Nq,Nk", [(128, 300, 100), (64, 129, 7)])
+def test_bwd_more_queries_than_keys_unmasked(d, Nq, Nk):
+    q, k, v, do = _inputs(11800 + Nq + d, 1, 8, 2, Nq, Nk, d)
+    scale = 1 / math.sqrt(d)
+    got = _run(q, k, v, do, False, scale)
+    ref = oa.attention_bwd(q, k, v, do, causal=False, scale=scale, dtype="bf16")
+    for name, a, r in zip(("dq", "dk", "dv"), got, ref):
+        _grad_check(a, r, f"bwd {name} unmasked Nq={Nq} > Nk={Nk} d={d}")
+
+
 def test_bwd_deterministic():
     q, k, v, do = _inputs(11400, 1, 8, 2, 257, 257, 128)
     a = _run(q, k, v, do, True, 0.0884, 10000.0)

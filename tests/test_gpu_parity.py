@@ -64,6 +64,18 @@ def test_small_ragged(dtype, d, Nq, Nk, causal):
     check(o, lse, ro, rl, dtype, f"{dtype} d={d} Nq={Nq} Nk={Nk} causal={causal}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Nq,Nk", [(300, 129), (129, 7), (65, 1)])
+def test_more_queries_than_keys_unmasked(dtype, d, Nq, Nk):
+    """No mask and more queries than keys (allowed without a mask or RoPE):
+    every query sees all Nk keys, including a single key."""
+    q, k, v = _small_inputs(12100 + Nq + Nk + d, 1, 4, 2, Nq, Nk, d, dtype)
+    o, lse = _run_fwd(q, k, v, dtype, False, 1 / math.sqrt(d), 0.0)
+    ro, rl = oa.attention(q, k, v, causal=False, scale=1 / math.sqrt(d), dtype=dtype)
+    check(o, lse, ro, rl, dtype, f"unmasked Nq={Nq} > Nk={Nk} d={d} {dtype}")
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 4), (8, 2), (8, 1), (16, 2), (12, 4), (6, 2), (3, 1)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_head_sharing(Hq, Hkv, dtype):
