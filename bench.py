@@ -311,8 +311,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="time one leg only (for profiling)")
+    ap.add_argument("--only", choices=["prefill", "decode", "backward"], default=None,
+                    help="time one leg only, or the backward pass alone (for profiling)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra prefill workloads (MHA d=64 N=2048, GQA N=32768, sliding window)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -341,6 +341,12 @@ def main():
     w4 = W.WORKLOADS["decode_b32"]
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    if args.only == "backward":
+        # attn_bwd on the prefill workload alone (for profiling): one untimed
+        # call, then --steps timed calls
+        rec = extra_backward(torch, esd, stream, w3, reps=args.steps)
+        print(json.dumps({"only": "backward", **rec}), flush=True)
+        return
 
     do_pf = args.only in (None, "prefill")
     do_dec = args.only in (None, "decode")
