@@ -11,6 +11,8 @@ Functions (same names as the C entry points):
       window=0)       (window > 0: attn_fwd_window, causal sliding window)
   bwd(q, k, v, o, lse, dout, causal, scale=None, rope_base=0.0, workspace=None)
   decode(q, k_cache, v_cache, seq_lens, scale=None, out=None, lse=None, workspace=None)
+  decode_noalloc(q, k_cache, v_cache, seq_lens, scale=None, out=None, lse=None)
+                      (no workspace: the library's static per-device array)
   decode_multi(q, k_cache, v_cache, seq_lens, scale=None, rope_base=0.0, out=None, lse=None,
                workspace=None)   (q [B,Hq,T,d]: T new tokens per sequence)
   decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale=None, rope_base=0.0, out=None,
@@ -38,7 +40,7 @@ EXPORTS = ("attn_status_str", "attn_fwd_workspace_bytes", "attn_fwd", "attn_fwd_
            "attn_bwd_workspace_bytes", "attn_bwd",
            "attn_decode_workspace_bytes", "attn_decode", "attn_decode_multi_workspace_bytes",
            "attn_decode_multi", "attn_decode_paged_workspace_bytes", "attn_decode_paged",
-           "attn_rope_apply")
+           "attn_rope_apply", "attn_decode_noalloc")
 
 _lib = None
 
@@ -85,6 +87,8 @@ def lib():
     L.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, f, i,
                                     vp, sz, vp]
     L.attn_decode_paged.restype = i
+    L.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    L.attn_decode_noalloc.restype = i
     L.attn_rope_apply.argtypes = [vp, vp, i, i, i, i, i, f, i, vp]
     L.attn_rope_apply.restype = i
     _lib = L
@@ -271,6 +275,36 @@ def decode(q, k_cache, v_cache, seq_lens, scale=None, out=None, lse=None, worksp
     _check("attn_decode", L.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
                                         _ptr(out), _ptr(lse), B, Hq, Hkv, max_len, d,
                                         float(scale), code, _ptr(workspace), wsb, _stream()))
+    return out, lse
+
+
+# Capacity of the library's static per-device array (ATTN_DECODE_NOALLOC_MAX_BYTES).
+DECODE_NOALLOC_MAX_BYTES = 16 << 20
+
+
+def decode_noalloc(q, k_cache, v_cache, seq_lens, scale=None, out=None, lse=None):
+    """``decode`` without a workspace (attn_decode_noalloc): the partial states
+    live in the library's static per-device array, so with ``out`` and ``lse``
+    given the call allocates nothing.  Calls that overlap on one device race."""
+    import torch
+    L = lib()
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
+        _need_cuda_contig(n, t)
+    if seq_lens.dtype != torch.int32:
+        raise TypeError("seq_lens must be int32")
+    B, Hq, d = q.shape
+    Bc, Hkv, max_len, dc = k_cache.shape
+    if (Bc, dc) != (B, d) or tuple(v_cache.shape) != tuple(k_cache.shape) or seq_lens.numel() != B:
+        raise ValueError("shape mismatch between q, caches and seq_lens")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check_out("out", out, (B, Hq, d), torch.float32)
+    _check_out("lse", lse, (B, Hq), torch.float32)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _check("attn_decode_noalloc", L.attn_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(out), _ptr(lse), B, Hq, Hkv,
+        max_len, d, float(scale), _dtype_code(q), _stream()))
     return out, lse
 
 

@@ -179,7 +179,7 @@ int decode_impl(const void* q, const void* k, const void* v, const int32_t* tabl
                 const int32_t* seq_lens, float* o, float* lse, int B, int Hq, int Hkv, int T,
                 int max_len, int num_blocks, int block_size, int max_blocks, int d, float scale,
                 float rope_base, attn_dtype dtype, void* workspace, size_t workspace_bytes,
-                hipStream_t stream) {
+                hipStream_t stream, bool use_scratch = false) {
     if (B < 0 || Hq < 0) return fail(ATTN_ERR_INVALID, "negative size");
     if (Hkv < 1 || T < 1 || max_len < 1 || d < 1)
         return fail(ATTN_ERR_INVALID, "Hkv, T, max_len and d must be >= 1");
@@ -200,6 +200,15 @@ int decode_impl(const void* q, const void* k, const void* v, const int32_t* tabl
         return fail(ATTN_ERR_INVALID, "q, caches and o must be 16-byte aligned");
     const int chunk = attn::decode_chunk(table != nullptr);
     const size_t need = decode_ws_bytes(B, Hq, Hkv, T, max_len, d, chunk);
+    if (use_scratch) {
+        // the partial states go to the library's static per-device array
+        if (need > attn::kNoAllocScratchBytes)
+            return fail(ATTN_ERR_WORKSPACE,
+                        "partial states exceed the static scratch (ATTN_DECODE_NOALLOC_MAX_BYTES)");
+        const hipError_t e = attn::noalloc_scratch(&workspace);
+        if (e != hipSuccess) return fail(ATTN_ERR_HIP, "static scratch address");
+        workspace_bytes = attn::kNoAllocScratchBytes;
+    }
     if (workspace == nullptr || workspace_bytes < need)
         return fail(ATTN_ERR_WORKSPACE, "decode workspace missing or too small");
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
@@ -273,6 +282,14 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 hipStream_t stream) {
     return attn_decode_multi(q, k_cache, v_cache, seq_lens, o, lse, B, Hq, Hkv, 1, max_len, d,
                              scale, 0.f, dtype, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seq_lens, float* o, float* lse,
+                        int B, int Hq, int Hkv, int max_len, int d, float scale,
+                        attn_dtype dtype, hipStream_t stream) {
+    return decode_impl(q, k_cache, v_cache, nullptr, seq_lens, o, lse, B, Hq, Hkv, 1, max_len,
+                       0, 1, 0, d, scale, 0.f, dtype, nullptr, 0, stream, /*use_scratch=*/true);
 }
 
 // Workspace of attn_bwd, in order (each section 256-byte aligned): dO in bf16

@@ -54,6 +54,8 @@
 //     fetches its (at most eight) table entries once, one per lane, and picks
 //     each instruction's entry with v_readlane.
 
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -499,6 +501,43 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// ---- the allocation-free decode entry point's partial states
+//
+// One fixed array per device holds the split kernel's partial states for
+// attn_decode_noalloc, so that call needs no allocation.  Host code never
+// passes the array's name to a kernel (on the host it only stands in for the
+// symbol); it uses the device address that hipGetSymbolAddress returns, once
+// per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+    *ptr = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    try {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (g_scratch_ptr[dev] == nullptr) {
+            void* p = nullptr;
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (p == nullptr) return hipErrorInvalidSymbol;
+            g_scratch_ptr[dev] = p;
+        }
+        *ptr = g_scratch_ptr[dev];
+    } catch (...) {
+        return hipErrorUnknown;
+    }
+    return hipSuccess;
+}
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
     if (a.B == 0 || a.Hq == 0) return hipSuccess;

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "attn.h"
+
 namespace attn {
 
 struct FwdArgs {
@@ -58,6 +60,14 @@ constexpr int kDecodeChunkPaged = 1024;
 constexpr int decode_chunk(bool paged) { return paged ? kDecodeChunkPaged : kDecodeChunk; }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+
+// Size of the per-device static array that holds attn_decode_noalloc's
+// partial states (ATTN_DECODE_NOALLOC_MAX_BYTES in attn.h).
+constexpr size_t kNoAllocScratchBytes = ATTN_DECODE_NOALLOC_MAX_BYTES;
+
+// Device address of the current device's copy of that array, looked up with
+// hipGetSymbolAddress on the first call per device.
+hipError_t noalloc_scratch(void** ptr);
 
 struct BwdArgs {
     const uint16_t* q;   // rotated Q when RoPE is on

@@ -172,6 +172,34 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 attn_dtype dtype, void* workspace, size_t workspace_bytes,
                 hipStream_t stream);
 
+/* Capacity of the static per-device array behind attn_decode_noalloc. */
+#define ATTN_DECODE_NOALLOC_MAX_BYTES ((size_t)16 << 20)
+
+/*
+ * attn_decode without a workspace argument, for callers that cannot allocate
+ * device memory at call time: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments (minus the
+ * workspace), arithmetic, results (bit for bit) and errors as attn_decode.
+ * The partial states live in one static array of ATTN_DECODE_NOALLOC_MAX_BYTES
+ * per device, part of the library's code object and held until the process
+ * ends; the call allocates nothing.
+ *   Limit: attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d) must be at most
+ *   ATTN_DECODE_NOALLOC_MAX_BYTES (e.g. B = 32, Hq = 32, max_len = 32768,
+ *   d = 128 needs 8.5 MB); larger sizes return ATTN_ERR_WORKSPACE before any
+ *   HIP call.
+ *   Sharing: every call on one device uses the same array and leaves its
+ *   contents behind (nothing in it needs to start at zero: the merge reads
+ *   only partial states the same call wrote).  Calls whose work overlaps on
+ *   one device (other streams, other threads, overlapping graph replays)
+ *   race on the array and give wrong results; order them.
+ * The first call on a device looks up the array's device address once
+ * (hipGetSymbolAddress); later calls make no HIP call besides the launches.
+ */
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seq_lens, float* o, float* lse,
+                        int B, int Hq, int Hkv, int max_len, int d, float scale,
+                        attn_dtype dtype, hipStream_t stream);
+
 /* Bytes of workspace attn_decode_multi needs: B*Hq*T*ceil(max_len/2048)
  * partial states of d + 1 floats (256-byte aligned split). */
 size_t attn_decode_multi_workspace_bytes(int B, int Hq, int Hkv, int T, int max_len, int d);

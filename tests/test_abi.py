@@ -116,6 +116,35 @@ def test_decode_rejects_on_host(kw, code):
     assert _dec(**kw) == code
 
 
+def _dec_noalloc(**kw):
+    a = dict(q=P, k=P, v=P, lens=P, o=P, lse=None, B=2, Hq=8, Hkv=2, max_len=64, d=128,
+             scale=0.1, dtype=esd.ATTN_BF16)
+    a.update(kw)
+    return esd.lib().attn_decode_noalloc(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"],
+                                         a["B"], a["Hq"], a["Hkv"], a["max_len"], a["d"],
+                                         a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lens=None), 1), (dict(k=None), 1), (dict(Hq=6, Hkv=4), 1), (dict(max_len=0), 1),
+    (dict(scale=float("nan")), 1), (dict(dtype=esd.ATTN_F32), 2), (dict(d=80), 2),
+    (dict(q=ctypes.c_void_p(258)), 1), (dict(max_len=1 << 23), 2),
+    # partial states past the static array: 64 * 32 rows x 17 chunks of 2048 keys
+    (dict(B=64, Hq=32, Hkv=8, max_len=34000), 4),
+])
+def test_decode_noalloc_rejects_on_host(kw, code):
+    assert _dec_noalloc(**kw) == code
+
+
+def test_decode_noalloc_limit_matches_workspace_sizes():
+    assert esd.decode_workspace_bytes(32, 32, 8, 32768, 128) <= esd.DECODE_NOALLOC_MAX_BYTES
+    assert esd.decode_workspace_bytes(64, 32, 8, 34000, 128) > esd.DECODE_NOALLOC_MAX_BYTES
+    hdr = open(os.path.join(ROOT, "include", "attn.h")).read()
+    assert "#define ATTN_DECODE_NOALLOC_MAX_BYTES ((size_t)16 << 20)" in hdr
+    assert esd.DECODE_NOALLOC_MAX_BYTES == 16 << 20
+    assert _dec_noalloc(B=0, q=None, k=None, v=None, lens=None, o=None) == 0
+
+
 def test_decode_empty_is_a_noop():
     assert _dec(B=0, q=None, k=None, v=None, lens=None, o=None, ws=None, wsb=0) == 0
 
