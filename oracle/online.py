@@ -1,20 +1,27 @@
 """Blocked online softmax and partial-state merge in fp64 (test infrastructure).
 
-These follow the recurrence exactly as the pages state it, one query row at a
-time, so the tests can pin the algebra the GPU kernels are built on:
+These model, one query row at a time, the algebra the GPU kernels are built
+on, so the tests can pin it:
 
-* ``online_row``: "coding-interview attention from scratch", section 三.7 and
-  "Attention mechanisms: from alignment to efficient long context", section 19:
-  keep the running max m, the running sum l of exp(s - m) and the running
-  weighted sum acc; when a block raises the max, multiply l and acc by
-  exp(m_old - m_new) before adding the block; at the end O = acc / l.  The
-  first block has m_old = -inf, whose factor is taken as 0.
+* ``partial``: the state (m, d, O) of one subset of keys, formed densely: m is
+  the largest score, d the sum of exp(s - m), O the d-normalised weighted sum
+  of the value rows.
 * ``merge``: "Transformer Architecture Breakdown", section 4.2 and
-  "Transformer Architecture Deconstructed", Online Softmax: two partial states
-  (m1, d1, O1) and (m2, d2, O2) of disjoint key sets combine with
+  "Transformer Architecture Deconstructed", Online Softmax: two states of
+  disjoint key sets combine by bringing both sums to the larger max,
   m = max(m1, m2), d = d1 e^(m1-m) + d2 e^(m2-m),
-  O = (d1 e^(m1-m) O1 + d2 e^(m2-m) O2) / d.  Applied pairwise, left to right,
-  to any number of parts.  A part with no visible key (m = -inf) contributes 0.
+  O = (d1 e^(m1-m) O1 + d2 e^(m2-m) O2) / d; applied pairwise, left to right,
+  to any number of parts.  A part with no visible key (m = -inf) contributes
+  nothing.
+* ``online_row``: the streaming form ("coding-interview attention from
+  scratch", section 三.7; "Attention mechanisms: from alignment to efficient
+  long context", section 19) as a left fold: the row's keys arrive in blocks,
+  and the running state absorbs each block's partial state with ``merge``.
+  The factor e^(m_old - m_new) that ``merge`` applies to the running state is
+  the rescale of the running sum and accumulator the pages describe.
+* ``online_row_uncorrected``: the same stream with that factor left out (each
+  block weighted against the running max, earlier sums never brought up to
+  date) -- the defect the pages warn about, kept so a test can show it wrong.
 
 Nothing here is imported by the GPU path; it models the algorithm only.
 """
@@ -26,31 +33,38 @@ import math
 import numpy as np
 
 
-def online_row(scores: np.ndarray, v: np.ndarray, block: int, *, rescale: bool = True):
-    """O and (m, l) of one query row from its scores [n] (-inf = masked) and V [n, d].
-
-    ``rescale=False`` drops the exp(m_old - m_new) correction: the defective
-    variant the pages warn about, kept so a test can show that it is wrong.
-    """
+def online_row(scores: np.ndarray, v: np.ndarray, block: int):
+    """O and (m, l) of one query row from its scores [n] (-inf = masked) and V [n, d],
+    reading the keys ``block`` at a time and folding each block's partial
+    state into the running one."""
     scores = np.asarray(scores, np.float64)
     v = np.asarray(v, np.float64)
-    m = -math.inf
-    l = 0.0
-    acc = np.zeros(v.shape[1])
+    state = (-math.inf, 0.0, np.zeros(v.shape[1]))
     for s0 in range(0, len(scores), block):
-        sb = scores[s0:s0 + block]
-        m_new = max(m, float(sb.max()))
-        if m_new == -math.inf:  # every key so far is masked
+        state = merge([state, partial(scores[s0:s0 + block], v[s0:s0 + block])])
+    m, l, o = state
+    return o, m, l
+
+
+def online_row_uncorrected(scores: np.ndarray, v: np.ndarray, block: int):
+    """The stream without the correction factor: every block's weights are taken
+    against the largest score seen so far, but what was summed before a larger
+    score arrived is not scaled down to it.  Exact only while the largest score
+    of the row sits in the first block."""
+    scores = np.asarray(scores, np.float64)
+    v = np.asarray(v, np.float64)
+    top = -math.inf
+    total = 0.0
+    weighted = np.zeros(v.shape[1])
+    for s0 in range(0, len(scores), block):
+        blk = scores[s0:s0 + block]
+        top = max(top, float(blk.max()))
+        if top == -math.inf:
             continue
-        if rescale:
-            alpha = math.exp(m - m_new) if m > -math.inf else 0.0
-        else:
-            alpha = 1.0
-        p = np.exp(sb - m_new)
-        l = l * alpha + float(p.sum())
-        acc = acc * alpha + p @ v[s0:s0 + block]
-        m = m_new
-    return acc / l, m, l
+        w = np.exp(blk - top)
+        total += float(w.sum())
+        weighted += w @ v[s0:s0 + block]
+    return weighted / total, top, total
 
 
 def partial(scores: np.ndarray, v: np.ndarray):

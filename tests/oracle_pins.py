@@ -589,19 +589,45 @@ def pin_backward_finite_differences():
 
 def pin_backward_rows_equal_full():
     """The row-sampled backward (rowsum(P * dP) taken as dO . O) equals the full
-    one on every sampled row, with and without RoPE."""
-    B, Hq, Hkv, Nq, Nk, d = 2, 4, 2, 9, 12, 8
-    for base, causal in ((0.0, True), (100.0, True), (0.0, False)):
-        q, k, v = _rand_inputs(440, B, Hq, Hkv, Nq, Nk, d, "bf16")
-        do = _rng(441).standard_normal((B, Hq, Nq, d))
+    one on every sampled row, with and without RoPE, for groups of 2 and 4 query
+    heads per KV head and fewer queries than keys (bottom-right positions)."""
+    cases = [
+        # B, Hq, Hkv, Nq, Nk, d, base, causal, (b, g), q rows, k rows
+        (2, 4, 2, 9, 12, 8, 0.0, True, (1, 1), [0, 4, 8], [0, 3, 11]),
+        (2, 4, 2, 9, 12, 8, 100.0, True, (1, 1), [0, 4, 8], [0, 3, 11]),
+        (2, 4, 2, 9, 12, 8, 0.0, False, (1, 1), [0, 4, 8], [0, 3, 11]),
+        (1, 8, 2, 7, 13, 8, 10000.0, True, (0, 1), [0, 3, 6], [0, 5, 6, 12]),
+        (2, 8, 2, 6, 10, 16, 500.0, False, (1, 0), [1, 5], [0, 9]),
+    ]
+    for n, (B, Hq, Hkv, Nq, Nk, d, base, causal, (b, g), qr, kr) in enumerate(cases):
+        q, k, v = _rand_inputs(440 + n, B, Hq, Hkv, Nq, Nk, d, "bf16")
+        do = _rng(441 + n).standard_normal((B, Hq, Nq, d))
         dq, dk, dv = oa.attention_bwd(q, k, v, do, causal=causal, scale=0.3, rope_base=base,
                                       dtype="bf16")
-        qr, kr = [0, 4, 8], [0, 3, 11]
-        sq, sk, sv = oa.attention_bwd_rows(q, k, v, do, 1, 1, qr, kr, causal=causal, scale=0.3,
+        G = Hq // Hkv
+        sq, sk, sv = oa.attention_bwd_rows(q, k, v, do, b, g, qr, kr, causal=causal, scale=0.3,
                                            rope_base=base, dtype="bf16")
-        assert np.max(np.abs(sq - dq[1, 2:4][:, qr])) < 1e-12
-        assert np.max(np.abs(sk - dk[1, 1, kr])) < 1e-12
-        assert np.max(np.abs(sv - dv[1, 1, kr])) < 1e-12
+        assert np.max(np.abs(sq - dq[b, g * G:(g + 1) * G][:, qr])) < 1e-12, n
+        assert np.max(np.abs(sk - dk[b, g, kr])) < 1e-12, n
+        assert np.max(np.abs(sv - dv[b, g, kr])) < 1e-12, n
+
+
+def pin_bf16_bits_decoding():
+    """Every one of the 65536 bf16 bit patterns is read as the value torch's
+    bfloat16 dtype gives the same bits (NaN patterns as NaN), and fp32 arrays
+    are widened unchanged.  Every GPU comparison reads its inputs this way."""
+    import torch
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):  # signalling NaN patterns warn on the cast
+        got = oa._f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signed zeros and infinities keep their sign
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    x = _rng(16).standard_normal(1000).astype(np.float32)
+    assert np.array_equal(oa._f64(x), x.astype(np.float64))
 
 
 ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

@@ -56,10 +56,10 @@ def test_no_rescale_is_wrong_unless_first_block_holds_max():
     r = np.random.default_rng(3)
     v = r.standard_normal((8, 3))
     rising = np.array([0.0, 0.1, 0.2, 0.3, 3.0, 3.1, 3.2, 3.3])
-    o_bad, _, _ = ol.online_row(rising, v, 4, rescale=False)
+    o_bad, _, _ = ol.online_row_uncorrected(rising, v, 4)
     assert np.max(np.abs(o_bad - _dense(rising, v)[0])) > 1e-3
     first = np.array([5.0, 0.1, 0.2, 0.3, 1.0, 1.1, 1.2, 1.3])
-    o_ok, _, _ = ol.online_row(first, v, 4, rescale=False)
+    o_ok, _, _ = ol.online_row_uncorrected(first, v, 4)
     assert np.max(np.abs(o_ok - _dense(first, v)[0])) < 1e-14
 
 

@@ -164,7 +164,28 @@ def _bwd_without_rowsum(q, k, v, do, *, causal, scale, rope_base=0.0, dtype="bf1
     return dq, dk, dv
 
 
+_orig_f64 = oa._f64
+
+
+def _f64_as_fp16(x):
+    # bf16 bits misread as IEEE half precision
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return x.view(np.float16).astype(np.float64)
+    return _orig_f64(x)
+
+
+def _bwd_rows_wrong_group(q, k, v, do, b, g, q_rows, k_rows, **kw):
+    # the query heads of the next KV head summed into this one's dK, dV
+    Hkv = k.shape[1]
+    return _orig_bwd_rows(q, k, v, do, b, (g + 1) % Hkv, q_rows, k_rows, **kw)
+
+
+_orig_bwd_rows = oa.attention_bwd_rows
+
 MUTATIONS = {
+    "bf16_bits_read_as_fp16": ("_f64", _f64_as_fp16),
+    "bwd_rows_wrong_group": ("attention_bwd_rows", _bwd_rows_wrong_group),
     "bwd_rope_not_transposed": ("rope_transpose", _rope_transpose_forward),
     "bwd_dropped_rowsum": ("attention_bwd", _bwd_without_rowsum),
     "paged_index_swapped": ("gather_paged", _gather_swapped),
