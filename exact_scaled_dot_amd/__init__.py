@@ -17,6 +17,9 @@ Functions (same names as the C entry points):
                workspace=None)   (q [B,Hq,T,d]: T new tokens per sequence)
   decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale=None, rope_base=0.0, out=None,
                lse=None, workspace=None)   (pools [num_blocks, Hkv, block_size, d])
+  prefill_cached(q, k_cache, v_cache, scale=None, rope_base=0.0, out=None, lse=None)
+                      (chunked prefill over a cache with keys stored rotated)
+  decode_multi, decode_paged and prefill_cached take out_dtype=torch.bfloat16 for a bf16 O
   rope_apply(x, rope_base, pos_offset=0, out=None)
   fwd_workspace_bytes(...), decode_workspace_bytes(...), decode_multi_workspace_bytes(...),
   decode_paged_workspace_bytes(...), status_str(code)
@@ -40,7 +43,7 @@ EXPORTS = ("attn_status_str", "attn_fwd_workspace_bytes", "attn_fwd", "attn_fwd_
            "attn_bwd_workspace_bytes", "attn_bwd",
            "attn_decode_workspace_bytes", "attn_decode", "attn_decode_multi_workspace_bytes",
            "attn_decode_multi", "attn_decode_paged_workspace_bytes", "attn_decode_paged",
-           "attn_rope_apply", "attn_decode_noalloc")
+           "attn_rope_apply", "attn_decode_noalloc", "attn_prefill_cached")
 
 _lib = None
 
@@ -80,12 +83,15 @@ def lib():
     L.attn_decode.restype = i
     L.attn_decode_multi_workspace_bytes.argtypes = [i, i, i, i, i, i]
     L.attn_decode_multi_workspace_bytes.restype = sz
-    L.attn_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, i, vp, sz, vp]
+    L.attn_prefill_cached.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, i, i, vp]
+    L.attn_prefill_cached.restype = i
+    L.attn_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, i, i, vp, sz,
+                                    vp]
     L.attn_decode_multi.restype = i
     L.attn_decode_paged_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     L.attn_decode_paged_workspace_bytes.restype = sz
     L.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, f, i,
-                                    vp, sz, vp]
+                                    i, vp, sz, vp]
     L.attn_decode_paged.restype = i
     L.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     L.attn_decode_noalloc.restype = i
@@ -146,6 +152,16 @@ def _check_out(name, t, shape, dtype):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
+def _out_code(dtype) -> int:
+    """Output dtype code: torch.float32 -> ATTN_F32, torch.bfloat16 -> ATTN_BF16."""
+    import torch
+    if dtype == torch.float32:
+        return ATTN_F32
+    if dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise TypeError(f"output dtype must be float32 or bfloat16, got {dtype}")
+
+
 def fwd_workspace_bytes(B, Hkv, Nk, d, rope_base, dtype_code) -> int:
     return int(lib().attn_fwd_workspace_bytes(B, Hkv, Nk, d, float(rope_base), dtype_code))
 
@@ -198,6 +214,38 @@ def fwd(q, k, v, causal: bool, scale=None, rope_base: float = 0.0, out=None, lse
     _check("attn_fwd", L.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv,
                                   Nq, Nk, d, int(bool(causal)), float(scale), float(rope_base),
                                   code, _ptr(workspace), wsb, _stream()))
+    return out, lse
+
+
+def prefill_cached(q, k_cache, v_cache, scale=None, rope_base: float = 0.0, out=None, lse=None,
+                   out_dtype=None, want_lse: bool = True):
+    """Chunked prefill (attn_prefill_cached): q [B,Hq,Nq,d] are the last Nq
+    positions of caches k_cache, v_cache [B,Hkv,Nk,d] whose keys are stored
+    already rotated; query i sits at Nk - Nq + i and sees keys up to there.
+    O is float32, or bfloat16 with out_dtype=torch.bfloat16."""
+    import torch
+    L = lib()
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _need_cuda_contig(n, t)
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q, k_cache, v_cache must share a dtype")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k_cache.shape
+    if (Bk, dk) != (B, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("shape mismatch between q and the caches")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out_dtype is None:
+        out_dtype = torch.float32 if out is None else out.dtype
+    _check_out("out", out, (B, Hq, Nq, d), out_dtype)
+    _check_out("lse", lse, (B, Hq, Nq), torch.float32)
+    if out is None:
+        out = torch.empty((B, Hq, Nq, d), dtype=out_dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check("attn_prefill_cached", L.attn_prefill_cached(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+        float(scale), float(rope_base), _dtype_code(q), _out_code(out_dtype), _stream()))
     return out, lse
 
 
@@ -309,9 +357,10 @@ def decode_noalloc(q, k_cache, v_cache, seq_lens, scale=None, out=None, lse=None
 
 
 def decode_multi(q, k_cache, v_cache, seq_lens, scale=None, rope_base: float = 0.0, out=None,
-                 lse=None, workspace=None, want_lse: bool = True):
+                 lse=None, workspace=None, want_lse: bool = True, out_dtype=None):
     """T new tokens per sequence (q [B,Hq,T,d]); token t of sequence b sits at
-    position seq_lens[b] - T + t and sees cache rows up to that position."""
+    position seq_lens[b] - T + t and sees cache rows up to that position.  O is
+    float32, or bfloat16 with out_dtype=torch.bfloat16."""
     import torch
     L = lib()
     for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
@@ -325,11 +374,13 @@ def decode_multi(q, k_cache, v_cache, seq_lens, scale=None, rope_base: float = 0
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    _check_out("out", out, (B, Hq, T, d), torch.float32)
+    if out_dtype is None:
+        out_dtype = torch.float32 if out is None else out.dtype
+    _check_out("out", out, (B, Hq, T, d), out_dtype)
     _check_out("lse", lse, (B, Hq, T), torch.float32)
     _check_out("workspace", workspace, None, torch.uint8)
     if out is None:
-        out = torch.empty((B, Hq, T, d), dtype=torch.float32, device=q.device)
+        out = torch.empty((B, Hq, T, d), dtype=out_dtype, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
     need = decode_multi_workspace_bytes(B, Hq, Hkv, T, max_len, d)
@@ -338,7 +389,8 @@ def decode_multi(q, k_cache, v_cache, seq_lens, scale=None, rope_base: float = 0
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("attn_decode_multi", L.attn_decode_multi(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(out), _ptr(lse), B, Hq, Hkv,
-        T, max_len, d, float(scale), float(rope_base), code, _ptr(workspace), wsb, _stream()))
+        T, max_len, d, float(scale), float(rope_base), code, _out_code(out_dtype), _ptr(workspace),
+        wsb, _stream()))
     return out, lse
 
 
@@ -347,7 +399,7 @@ def decode_paged_workspace_bytes(B, Hq, Hkv, T, max_blocks, block_size, d) -> in
 
 
 def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale=None, rope_base: float = 0.0,
-                 out=None, lse=None, workspace=None, want_lse: bool = True):
+                 out=None, lse=None, workspace=None, want_lse: bool = True, out_dtype=None):
     """decode_multi over a paged cache: token p of sequence b is row p % block_size
     of pool block block_table[b, p // block_size]."""
     import torch
@@ -366,11 +418,13 @@ def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale=None, rope_base
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    _check_out("out", out, (B, Hq, T, d), torch.float32)
+    if out_dtype is None:
+        out_dtype = torch.float32 if out is None else out.dtype
+    _check_out("out", out, (B, Hq, T, d), out_dtype)
     _check_out("lse", lse, (B, Hq, T), torch.float32)
     _check_out("workspace", workspace, None, torch.uint8)
     if out is None:
-        out = torch.empty((B, Hq, T, d), dtype=torch.float32, device=q.device)
+        out = torch.empty((B, Hq, T, d), dtype=out_dtype, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
     need = decode_paged_workspace_bytes(B, Hq, Hkv, T, max_blocks, block_size, d)
@@ -380,7 +434,7 @@ def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale=None, rope_base
     _check("attn_decode_paged", L.attn_decode_paged(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), _ptr(out),
         _ptr(lse), B, Hq, Hkv, T, num_blocks, block_size, max_blocks, d, float(scale),
-        float(rope_base), code, _ptr(workspace), wsb, _stream()))
+        float(rope_base), code, _out_code(out_dtype), _ptr(workspace), wsb, _stream()))
     return out, lse
 
 

@@ -61,10 +61,13 @@ size_t attn_fwd_workspace_bytes(int B, int Hkv, int Nk, int d, float rope_base, 
 namespace {
 
 // Shared body of attn_fwd (window = 0) and attn_fwd_window (window >= 1, causal).
-int fwd_impl(const void* q, const void* k, const void* v, float* o, float* lse,
+// rotate_k: with RoPE, K is rotated into the workspace first (attn_fwd);
+// otherwise K is used as given (keys stored already rotated, attn_prefill_cached).
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int window,
              float scale, float rope_base, attn_dtype dtype,
-             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+             void* workspace, size_t workspace_bytes, hipStream_t stream,
+             bool rotate_k = true, attn_dtype o_dtype = ATTN_F32) {
     if (B < 0 || Hq < 0 || Nq < 0) return fail(ATTN_ERR_INVALID, "negative size");
     if (Hkv < 1 || Nk < 1 || d < 1) return fail(ATTN_ERR_INVALID, "Hkv, Nk and d must be >= 1");
     if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID, "Hq must be a multiple of Hkv");
@@ -77,6 +80,7 @@ int fwd_impl(const void* q, const void* k, const void* v, float* o, float* lse,
     if (rope_base != 0.f && Nq > Nk)
         return fail(ATTN_ERR_INVALID, "RoPE needs Nq <= Nk (query positions Nk-Nq+i must be >= 0)");
     if (!known_dtype(dtype)) return fail(ATTN_ERR_INVALID, "unknown dtype");
+    if (!known_dtype(o_dtype)) return fail(ATTN_ERR_INVALID, "unknown output dtype");
     if (!supported_d(d)) return fail(ATTN_ERR_UNSUPPORTED, "head dim must be 64 or 128");
     if ((long long)Nk * d * 4 >= (1LL << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "one head's K (or V) must be under 2 GiB (32-bit buffer offsets)");
@@ -85,7 +89,7 @@ int fwd_impl(const void* q, const void* k, const void* v, float* o, float* lse,
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return fail(ATTN_ERR_INVALID, "q, k, v, o must be 16-byte aligned");
     const bool rope = rope_base > 0.f;
-    const size_t need = attn_fwd_workspace_bytes(B, Hkv, Nk, d, rope_base, dtype);
+    const size_t need = rotate_k ? attn_fwd_workspace_bytes(B, Hkv, Nk, d, rope_base, dtype) : 0;
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
         return fail(ATTN_ERR_WORKSPACE, "workspace missing or too small for the rotated K");
     if (need > 0 && !aligned16(workspace)) return fail(ATTN_ERR_INVALID, "workspace must be 16-byte aligned");
@@ -95,6 +99,7 @@ int fwd_impl(const void* q, const void* k, const void* v, float* o, float* lse,
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.d = d;
     a.causal = causal; a.scale = scale; a.rope_tab = nullptr;
     a.window = window < Nk ? window : 0;  // a window covering every key is plain causal
+    a.o_bf16 = o_dtype == ATTN_BF16 ? 1 : 0;
 
     if (rope) {
         int dev = 0;
@@ -102,16 +107,18 @@ int fwd_impl(const void* q, const void* k, const void* v, float* o, float* lse,
         if (e != hipSuccess) return fail(ATTN_ERR_HIP, "hipGetDevice");
         const double2* tab = attn::rope_table(dev, rope_base, d, Nk, &e);
         if (!tab) return fail(ATTN_ERR_HIP, "RoPE table");
-        // K rotated once into the workspace; Q is rotated as it is loaded.
-        const long long rows = (long long)B * Hkv * Nk;
-        if (dtype == ATTN_BF16)
-            e = attn::launch_rope_bf16(static_cast<const uint16_t*>(k), static_cast<uint16_t*>(workspace),
-                                       rows, Nk, d, 0, tab, stream);
-        else
-            e = attn::launch_rope_f32(static_cast<const float*>(k), static_cast<float*>(workspace),
-                                      rows, Nk, d, 0, tab, stream);
-        if (e != hipSuccess) return fail(ATTN_ERR_HIP, "rope launch");
-        a.k = workspace;
+        if (rotate_k) {
+            // K rotated once into the workspace; Q is rotated as it is loaded.
+            const long long rows = (long long)B * Hkv * Nk;
+            if (dtype == ATTN_BF16)
+                e = attn::launch_rope_bf16(static_cast<const uint16_t*>(k), static_cast<uint16_t*>(workspace),
+                                           rows, Nk, d, 0, tab, stream);
+            else
+                e = attn::launch_rope_f32(static_cast<const float*>(k), static_cast<float*>(workspace),
+                                          rows, Nk, d, 0, tab, stream);
+            if (e != hipSuccess) return fail(ATTN_ERR_HIP, "rope launch");
+            a.k = workspace;
+        }
         a.rope_tab = tab;
     }
     hipError_t e = dtype == ATTN_BF16 ? attn::launch_prefill_bf16(a, stream)
@@ -139,6 +146,13 @@ int attn_fwd_window(const void* q, const void* k, const void* v, float* o, float
     if (window < 1) return fail(ATTN_ERR_INVALID, "window must be >= 1");
     return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, 1, window, scale, rope_base, dtype,
                     workspace, workspace_bytes, stream);
+}
+
+int attn_prefill_cached(const void* q, const void* k_cache, const void* v_cache, void* o,
+                        float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                        float rope_base, attn_dtype dtype, attn_dtype o_dtype, hipStream_t stream) {
+    return fwd_impl(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Nq, Nk, d, 1, 0, scale, rope_base,
+                    dtype, nullptr, 0, stream, /*rotate_k=*/false, o_dtype);
 }
 
 // Partial states of the split decode: one per (row, chunk of `chunk` keys),
@@ -176,10 +190,10 @@ namespace {
 // caches [B, Hkv, max_len, d]; otherwise pools [num_blocks, Hkv, block_size, d]
 // addressed through table [B, max_blocks] (max_len = max_blocks * block_size).
 int decode_impl(const void* q, const void* k, const void* v, const int32_t* table,
-                const int32_t* seq_lens, float* o, float* lse, int B, int Hq, int Hkv, int T,
+                const int32_t* seq_lens, void* o, float* lse, int B, int Hq, int Hkv, int T,
                 int max_len, int num_blocks, int block_size, int max_blocks, int d, float scale,
-                float rope_base, attn_dtype dtype, void* workspace, size_t workspace_bytes,
-                hipStream_t stream, bool use_scratch = false) {
+                float rope_base, attn_dtype dtype, attn_dtype o_dtype, void* workspace,
+                size_t workspace_bytes, hipStream_t stream, bool use_scratch = false) {
     if (B < 0 || Hq < 0) return fail(ATTN_ERR_INVALID, "negative size");
     if (Hkv < 1 || T < 1 || max_len < 1 || d < 1)
         return fail(ATTN_ERR_INVALID, "Hkv, T, max_len and d must be >= 1");
@@ -188,6 +202,7 @@ int decode_impl(const void* q, const void* k, const void* v, const int32_t* tabl
     if (rope_base != 0.f && !(std::isfinite(rope_base) && rope_base > 0.f))
         return fail(ATTN_ERR_INVALID, "rope_base must be 0 or a finite positive base");
     if (!known_dtype(dtype)) return fail(ATTN_ERR_INVALID, "unknown dtype");
+    if (!known_dtype(o_dtype)) return fail(ATTN_ERR_INVALID, "unknown output dtype");
     if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode is built for bf16");
     if (!supported_d(d)) return fail(ATTN_ERR_UNSUPPORTED, "head dim must be 64 or 128");
     if ((long long)max_len * d * 2 >= (1LL << 31))
@@ -220,6 +235,7 @@ int decode_impl(const void* q, const void* k, const void* v, const int32_t* tabl
     a.v = static_cast<const uint16_t*>(v);
     a.lens = seq_lens;
     a.o = o; a.lse = lse;
+    a.o_bf16 = o_dtype == ATTN_BF16 ? 1 : 0;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.T = T; a.max_len = max_len; a.d = d; a.scale = scale;
     a.rope_tab = nullptr;
     a.table = table;
@@ -250,19 +266,21 @@ int decode_impl(const void* q, const void* k, const void* v, const int32_t* tabl
 extern "C" {
 
 int attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
-                      const int32_t* seq_lens, float* o, float* lse,
+                      const int32_t* seq_lens, void* o, float* lse,
                       int B, int Hq, int Hkv, int T, int max_len, int d, float scale,
-                      float rope_base, attn_dtype dtype, void* workspace,
+                      float rope_base, attn_dtype dtype, attn_dtype o_dtype, void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
     return decode_impl(q, k_cache, v_cache, nullptr, seq_lens, o, lse, B, Hq, Hkv, T, max_len,
-                       0, 1, 0, d, scale, rope_base, dtype, workspace, workspace_bytes, stream);
+                       0, 1, 0, d, scale, rope_base, dtype, o_dtype, workspace, workspace_bytes,
+                       stream);
 }
 
 int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
-                      const int32_t* block_table, const int32_t* seq_lens, float* o, float* lse,
+                      const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
                       int B, int Hq, int Hkv, int T, int num_blocks, int block_size,
                       int max_blocks, int d, float scale, float rope_base, attn_dtype dtype,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                      attn_dtype o_dtype, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
     if (num_blocks < 1 || max_blocks < 1)
         return fail(ATTN_ERR_INVALID, "num_blocks and max_blocks must be >= 1");
     if (block_size < 16 || block_size > 4096 || (block_size & (block_size - 1)) != 0)
@@ -272,7 +290,7 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
     if (B > 0 && Hq > 0 && block_table == nullptr) return fail(ATTN_ERR_INVALID, "null block table");
     return decode_impl(q, k_pool, v_pool, block_table, seq_lens, o, lse, B, Hq, Hkv, T,
                        max_blocks * block_size, num_blocks, block_size, max_blocks, d, scale,
-                       rope_base, dtype, workspace, workspace_bytes, stream);
+                       rope_base, dtype, o_dtype, workspace, workspace_bytes, stream);
 }
 
 int attn_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -281,7 +299,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 attn_dtype dtype, void* workspace, size_t workspace_bytes,
                 hipStream_t stream) {
     return attn_decode_multi(q, k_cache, v_cache, seq_lens, o, lse, B, Hq, Hkv, 1, max_len, d,
-                             scale, 0.f, dtype, workspace, workspace_bytes, stream);
+                             scale, 0.f, dtype, ATTN_F32, workspace, workspace_bytes, stream);
 }
 
 int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
@@ -289,7 +307,8 @@ int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
                         int B, int Hq, int Hkv, int max_len, int d, float scale,
                         attn_dtype dtype, hipStream_t stream) {
     return decode_impl(q, k_cache, v_cache, nullptr, seq_lens, o, lse, B, Hq, Hkv, 1, max_len,
-                       0, 1, 0, d, scale, 0.f, dtype, nullptr, 0, stream, /*use_scratch=*/true);
+                       0, 1, 0, d, scale, 0.f, dtype, ATTN_F32, nullptr, 0, stream,
+                       /*use_scratch=*/true);
 }
 
 // Workspace of attn_bwd, in order (each section 256-byte aligned): dO in bf16

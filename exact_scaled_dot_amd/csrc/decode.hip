@@ -391,9 +391,9 @@ decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 template <int D>
 __global__ void __launch_bounds__(256)
 decode_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
-                    const int32_t* __restrict__ lens, float* __restrict__ o,
+                    const int32_t* __restrict__ lens, void* __restrict__ o,
                     float* __restrict__ lse, int Hq, int T, int max_len, int nchunks,
-                    int kCh) {
+                    int kCh, int o_bf16) {
     constexpr int NSPLIT = 256 / D;
     __shared__ float wts[1024];
     __shared__ float red[8];
@@ -408,8 +408,16 @@ decode_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
     len = len < 0 ? 0 : (len > max_len ? max_len : len);
     const int nvis = max(0, len - T + t + 1);  // keys 0 .. len-T+t
     const int nc = (nvis + kCh - 1) / kCh;
+    // O as fp32, or rounded to the nearest bf16 (even on ties)
+    auto store_o = [&](int dd, float x) {
+        if (o_bf16) {
+            static_cast<uint16_t*>(o)[(size_t)bh * D + dd] = (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu);
+        } else {
+            static_cast<float*>(o)[(size_t)bh * D + dd] = x;
+        }
+    };
     if (nc == 0) {  // no visible key: empty sum
-        if (tid < D) o[(size_t)bh * D + tid] = 0.f;
+        if (tid < D) store_o(tid, 0.f);
         if (lse != nullptr && tid == 0) lse[bh] = -INFINITY;
         return;
     }
@@ -460,7 +468,7 @@ decode_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
         float t = 0.f;
 #pragma unroll
         for (int i = 0; i < NSPLIT; ++i) t += part[i][tid];
-        o[(size_t)bh * D + tid] = t / wsum;
+        store_o(tid, t / wsum);
         if (lse != nullptr && tid == 0) lse[bh] = (M + fast_log2(wsum)) * kLn2;
     }
 }
@@ -496,7 +504,7 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     const long long rows = (long long)a.B * a.Hq * a.T;
     if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     decode_merge_kernel<D><<<(unsigned)rows, 256, 0, stream>>>(
-        a.ws_o, a.ws_lse, a.lens, a.o, a.lse, a.Hq, a.T, a.max_len, a.nchunks, a.chunk);
+        a.ws_o, a.ws_lse, a.lens, a.o, a.lse, a.Hq, a.T, a.max_len, a.nchunks, a.chunk, a.o_bf16);
     return hipGetLastError();
 }
 

@@ -14,13 +14,14 @@ struct FwdArgs {
     const void* q;
     const void* k;  // rotated K when RoPE is on
     const void* v;
-    float* o;
+    void* o;        // fp32, or bf16 when o_bf16
     float* lse;
     int B, Hq, Hkv, Nq, Nk, d;
     int causal;
     int window;  // > 0: causal sliding window of this many keys; 0: none
     float scale;
     const double2* rope_tab;  // null: no RoPE on Q
+    int o_bf16;               // 1: O stored as bf16 (nearest even from the fp32 value)
 };
 
 hipError_t launch_prefill_bf16(const FwdArgs& a, hipStream_t stream);
@@ -37,7 +38,7 @@ struct DecodeArgs {
     const uint16_t* k;
     const uint16_t* v;
     const int32_t* lens;
-    float* o;
+    void* o;        // fp32, or bf16 when o_bf16
     float* lse;
     int B, Hq, Hkv, T, max_len, d;  // T new query tokens per sequence
     float scale;
@@ -50,6 +51,7 @@ struct DecodeArgs {
     float* ws_lse;  // [B, Hq, T, nchunks] (log2 domain)
     int nchunks;
     int chunk;      // keys per split workgroup (decode_chunk(paged))
+    int o_bf16;     // 1: O stored as bf16 (nearest even from the fp32 value)
 };
 
 // Keys per split workgroup: 2048 for a contiguous cache (half the partial

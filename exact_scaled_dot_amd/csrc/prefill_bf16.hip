@@ -82,10 +82,10 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
 template <int D, bool CAUSAL, bool ROPE, bool WINDOW>
 __global__ void __launch_bounds__(waves_for<D>() * 64, 1)
 prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                    const uint16_t* __restrict__ v, float* __restrict__ o,
+                    const uint16_t* __restrict__ v, void* __restrict__ o,
                     float* __restrict__ lse, int B, int Hq, int Hkv, int Nq, int Nk,
                     float scale_log2, const double2* __restrict__ tab, int hpw, int wph,
-                    int nchunks, int nrb, int win) {
+                    int nchunks, int nrb, int win, int o_bf16) {
     static_assert(!WINDOW || CAUSAL, "the sliding window is built for causal attention");
     constexpr int kWaves = waves_for<D>();
     constexpr int KS = D + kKPad;       // K row stride in LDS (elements)
@@ -195,6 +195,10 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     float m_run = -INFINITY;   // reference max (log2 domain) of this lane's row
     float l_run = 0.f;         // this lane's share of the row sum (fp32 weights): for lse
     float r_run = 0.f;         // same sum of the bf16-rounded weights the MFMA used: for O
+    // refreshed only when the reference moves: -m (0 while m is -inf), and the
+    // raw row max above which the reference moves, (m + kLazy) / (scale log2 e)
+    float neg_m = 0.f;
+    float grow_at = -INFINITY;
 
     // transposed-read addressing for the V operand (A of O^T += V^T P^T)
     const int grp = lane >> 4;          // 16-lane group
@@ -216,17 +220,23 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                                (WINDOW && key0 < wave_lo);
         if (need_mask) {
             keep_branch();
+            // element i holds key kl + c_i with c_i = 8 (i / 4) + i % 4: one
+            // per-lane bound on c_i instead of a key per element
+            const int kl = key0 + 4 * half;
+            const int hi = (CAUSAL ? min(qpos, Nk - 1) : Nk - 1) - kl;
+            const int lo = WINDOW ? qpos - win + 1 - kl : 0;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int key = key0 + 8 * (i >> 2) + 4 * half + (i & 3);
-                const bool vis = (key < Nk) && (!CAUSAL || key <= qpos) &&
-                                 (!WINDOW || key > qpos - win);
+                const int ci = 8 * (i >> 2) + (i & 3);
+                const bool vis = ci <= hi && (!WINDOW || ci >= lo);
                 sc[i] = vis ? sc[i] : -INFINITY;
             }
         }
-        float mx = -INFINITY;
+        // row max as one chain of three-input maxima (v_max3_f32)
+        float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sc[i], sc[i + 1]));
+        for (int i = 3; i + 1 < 16; i += 2) mx = fmaxf(fmaxf(mx, sc[i]), sc[i + 1]);
+        mx = fmaxf(mx, sc[15]);
         {
             // the other half's max: v_permlane32_swap gives lanes 0-31 (r[0])
             // and lanes 32-63 (r[1]) in both halves, with no LDS round trip
@@ -238,20 +248,19 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             asm volatile("" : "+v"(lo), "+v"(hi));
             mx = fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
         }
-        const float m_cand = mx * scale_log2;
-        const bool grow = m_cand > m_run + kLazy;
+        const bool grow = mx > grow_at;
         if (__ballot(grow)) {
             keep_branch();
-            const float m_new = grow ? m_cand : m_run;
+            const float m_new = grow ? mx * scale_log2 : m_run;
             const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
             l_run *= alpha;
             r_run *= alpha;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
             m_run = m_new;
+            neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+            grow_at = (m_run + kLazy) / scale_log2;
         }
-        const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
-        float psum = 0.f;
         // the weights are the one stretch of pure vector work: raising the
         // wave's issue priority here lets it finish them while the other waves
         // of the SIMD keep the matrix cores fed (measured +1.5%; raising it
@@ -264,7 +273,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 p[e] = fast_exp2(fmaf(sc[8 * ss + e], scale_log2, neg_m));
-                psum += p[e];
+                l_run += p[e];
             }
             pw[ss].x = pack_bf16x2(p[0], p[1]);
             pw[ss].y = pack_bf16x2(p[2], p[3]);
@@ -275,7 +284,6 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             r_run = sum_bf16x2(pw[ss].z, r_run);
             r_run = sum_bf16x2(pw[ss].w, r_run);
         }
-        l_run += psum;
         __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int ss = 0; ss < 2; ++ss) {
@@ -324,7 +332,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float r_tot = r_run + __shfl_xor(r_run, 32);
     const float inv = 1.f / r_tot;
-    float* orow = o + (((size_t)b * Hq + hq) * Nq + qi) * D;
+    const size_t orow = (((size_t)b * Hq + hq) * Nq + qi) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -332,7 +340,11 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             const int d = 32 * db + 8 * i4 + 4 * half;
             float4 r = make_float4(oacc[db][4 * i4 + 0] * inv, oacc[db][4 * i4 + 1] * inv,
                                    oacc[db][4 * i4 + 2] * inv, oacc[db][4 * i4 + 3] * inv);
-            *reinterpret_cast<float4*>(orow + d) = r;
+            if (o_bf16)  // the fp32 value rounded to the nearest bf16 (even on ties)
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(o) + orow + d) =
+                    make_uint2(pack_bf16x2(r.x, r.y), pack_bf16x2(r.z, r.w));
+            else
+                *reinterpret_cast<float4*>(static_cast<float*>(o) + orow + d) = r;
         }
     }
     if (lse != nullptr && half == 0)
@@ -359,7 +371,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     prefill_bf16_kernel<D, CAUSAL, ROPE, WINDOW><<<(unsigned)nwg, kWaves * 64, 0, stream>>>(
         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
         static_cast<const uint16_t*>(a.v), a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, scale_log2,
-        a.rope_tab, hpw, wph, nchunks, nrb, WINDOW ? a.window : 0);
+        a.rope_tab, hpw, wph, nchunks, nrb, WINDOW ? a.window : 0, a.o_bf16);
     return hipGetLastError();
 }
 

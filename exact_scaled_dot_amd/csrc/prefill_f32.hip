@@ -21,9 +21,9 @@ constexpr int kBcF = 32;     // keys per tile
 template <int D, bool CAUSAL, bool ROPE, bool WINDOW>
 __global__ void __launch_bounds__(kRowsF)
 prefill_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
-                   const float* __restrict__ v, float* __restrict__ o, float* __restrict__ lse,
+                   const float* __restrict__ v, void* __restrict__ o, float* __restrict__ lse,
                    int B, int Hq, int Hkv, int Nq, int Nk, float scale_log2,
-                   const double2* __restrict__ tab, int nrb, int win) {
+                   const double2* __restrict__ tab, int nrb, int win, int o_bf16) {
     static_assert(!WINDOW || CAUSAL, "the sliding window is built for causal attention");
     __shared__ __attribute__((aligned(16))) float Ks[kBcF * D];
     __shared__ __attribute__((aligned(16))) float Vs[kBcF * D];
@@ -117,11 +117,17 @@ prefill_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
     }
     if (!ok) return;
     const float inv = 1.f / l_run;
-    float* orow = o + (((size_t)b * Hq + hq) * Nq + qi) * D;
+    const size_t orow = (((size_t)b * Hq + hq) * Nq + qi) * D;
 #pragma unroll
-    for (int d0 = 0; d0 < D; d0 += 4)
-        *reinterpret_cast<float4*>(orow + d0) =
-            make_float4(acc[d0] * inv, acc[d0 + 1] * inv, acc[d0 + 2] * inv, acc[d0 + 3] * inv);
+    for (int d0 = 0; d0 < D; d0 += 4) {
+        const float4 r = make_float4(acc[d0] * inv, acc[d0 + 1] * inv, acc[d0 + 2] * inv,
+                                     acc[d0 + 3] * inv);
+        if (o_bf16)  // the fp32 value rounded to the nearest bf16 (even on ties)
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(o) + orow + d0) =
+                make_uint2(pack_bf16x2(r.x, r.y), pack_bf16x2(r.z, r.w));
+        else
+            *reinterpret_cast<float4*>(static_cast<float*>(o) + orow + d0) = r;
+    }
     if (lse != nullptr) lse[((size_t)b * Hq + hq) * Nq + qi] = (m_run + fast_log2(l_run)) * kLn2;
 }
 
@@ -135,7 +141,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     prefill_f32_kernel<D, CAUSAL, ROPE, WINDOW><<<(unsigned)nwg, kRowsF, 0, stream>>>(
         static_cast<const float*>(a.q), static_cast<const float*>(a.k),
         static_cast<const float*>(a.v), a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, scale_log2,
-        a.rope_tab, nrb, WINDOW ? a.window : 0);
+        a.rope_tab, nrb, WINDOW ? a.window : 0, a.o_bf16);
     return hipGetLastError();
 }
 

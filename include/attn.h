@@ -18,6 +18,7 @@
  * Layouts (all contiguous, head dimension fastest, 64-bit offsets inside):
  *   q   [B, Hq,  Nq, d]      k, v [B, Hkv, Nk, d]     (dtype of the call)
  *   o   [B, Hq,  Nq, d] fp32 lse  [B, Hq, Nq] fp32 natural-log logsumexp
+ *   (the chunked-prefill and multi-token decode calls can store O as bf16)
  *   Query head h reads KV head h / (Hq / Hkv): MHA (Hkv = Hq), GQA, MQA
  *   (Hkv = 1) ("coding-interview attention from scratch", 三.4).
  *
@@ -112,6 +113,30 @@ int attn_fwd_window(const void* q, const void* k, const void* v, float* o, float
                     int B, int Hq, int Hkv, int Nq, int Nk, int d, int window,
                     float scale, float rope_base, attn_dtype dtype,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Chunked prefill against a KV cache ("coding-interview attention from
+ * scratch", section 八 question 5: Nq new tokens over a cache whose last Nq rows
+ * are their own K/V; the score block is all visible over the earlier rows and
+ * lower-triangular over the new ones).  Query i sits at position Nk - Nq + i
+ * and sees keys 0 .. Nk - Nq + i (attn_fwd's causal bottom-right rule).  The
+ * cached keys are used as given: with RoPE they are stored already rotated
+ * (as attn_decode_multi assumes), and only the queries are rotated, each at its
+ * own position, exactly as attn_fwd rotates Q.  So attn_prefill_cached on keys
+ * from attn_rope_apply(k, rope_base, 0) equals attn_fwd(causal = 1) on k, bit
+ * for bit (it runs the same attention kernel, without the rotation pass of K).
+ *   q          device [B, Hq, Nq, d], dtype.
+ *   k_cache, v_cache  device [B, Hkv, Nk, d], dtype; Nq <= Nk.
+ *   o          device [B, Hq, Nq, d]: fp32 when o_dtype = ATTN_F32, bf16 when
+ *              ATTN_BF16 (each element the fp32 result rounded to the nearest
+ *              bf16, ties to even).
+ *   lse        device fp32 [B, Hq, Nq] or NULL.
+ *   scale, rope_base, dtype: as attn_fwd.  No workspace is needed.
+ * Errors as attn_fwd with causal = 1; an unknown o_dtype is ATTN_ERR_INVALID.
+ */
+int attn_prefill_cached(const void* q, const void* k_cache, const void* v_cache, void* o,
+                        float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                        float rope_base, attn_dtype dtype, attn_dtype o_dtype, hipStream_t stream);
 
 /* Bytes of workspace attn_bwd needs: dO in bf16 and two fp32 values per query
  * row, plus the rotated Q and K (bf16) when rope_base > 0; 0 for fp32. */
@@ -217,7 +242,10 @@ size_t attn_decode_multi_workspace_bytes(int B, int Hq, int Hkv, int T, int max_
  *   k_cache, v_cache  device [B, Hkv, max_len, d] bf16, keys stored already
  *              rotated when RoPE is used; rows past seq_lens[b] are never read.
  *   seq_lens   device int32 [B].
- *   o          device fp32 [B, Hq, T, d];  lse  device fp32 [B, Hq, T] or NULL.
+ *   o          device [B, Hq, T, d]: fp32 when o_dtype = ATTN_F32, bf16 when
+ *              ATTN_BF16 (the fp32 result rounded to the nearest bf16, ties to
+ *              even; tokens without keys get 0).
+ *   lse        device fp32 [B, Hq, T] or NULL.
  *   rope_base  0 = queries used as given, else each query is rotated at its
  *              own position (fp64, rounded to bf16) as attn_fwd rotates Q.
  *   workspace  device buffer of attn_decode_multi_workspace_bytes(...) bytes,
@@ -229,9 +257,9 @@ size_t attn_decode_multi_workspace_bytes(int B, int Hq, int Hkv, int T, int max_
  * fit in 31 bits.
  */
 int attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
-                      const int32_t* seq_lens, float* o, float* lse,
+                      const int32_t* seq_lens, void* o, float* lse,
                       int B, int Hq, int Hkv, int T, int max_len, int d, float scale,
-                      float rope_base, attn_dtype dtype, void* workspace,
+                      float rope_base, attn_dtype dtype, attn_dtype o_dtype, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace attn_decode_paged needs: B*Hq*T*ceil(max_len/1024)
@@ -257,17 +285,19 @@ size_t attn_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int T, int max_
  *   seq_lens   device int32 [B], clamped to [0, max_blocks * block_size].  Rows
  *              at or past seq_lens[b] inside its last block are never read.
  *   block_size power of two in [16, 4096] (16 is the usual choice).
- *   o, lse, T, scale, rope_base, dtype, workspace: as attn_decode_multi, with
- *              attn_decode_paged_workspace_bytes(...) bytes of workspace.
+ *   o, lse, T, scale, rope_base, dtype, o_dtype, workspace: as
+ *              attn_decode_multi, with attn_decode_paged_workspace_bytes(...)
+ *              bytes of workspace.
  * Errors: num_blocks or max_blocks < 1, or a null table -> ATTN_ERR_INVALID;
  * another block_size, or max_blocks * block_size * d * 2 >= 2^31 ->
  * ATTN_ERR_UNSUPPORTED; otherwise as attn_decode_multi.
  */
 int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
-                      const int32_t* block_table, const int32_t* seq_lens, float* o, float* lse,
+                      const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
                       int B, int Hq, int Hkv, int T, int num_blocks, int block_size,
                       int max_blocks, int d, float scale, float rope_base, attn_dtype dtype,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+                      attn_dtype o_dtype, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
 
 /*
  * RoPE on its own: out[b,h,n,:] = rotate(x[b,h,n,:], position pos_offset + n),

@@ -97,6 +97,28 @@ def test_fwd_empty_is_a_noop(kw):
     assert _fwd(q=None, k=None, v=None, o=None, **kw) == 0
 
 
+def _pfc(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Hq=4, Hkv=2, Nq=8, Nk=8, d=64, scale=0.125,
+             rope=0.0, dtype=esd.ATTN_BF16, odt=esd.ATTN_F32)
+    a.update(kw)
+    return esd.lib().attn_prefill_cached(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                                         a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"], a["rope"],
+                                         a["dtype"], a["odt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(Hq=6, Hkv=4), 1), (dict(Nq=9, Nk=8), 1),
+    (dict(Nk=0), 1), (dict(scale=0.0), 1), (dict(rope=-1.0), 1), (dict(dtype=7), 1),
+    (dict(odt=2), 1), (dict(d=96), 2), (dict(o=ctypes.c_void_p(264)), 1),
+])
+def test_prefill_cached_rejects_on_host(kw, code):
+    assert _pfc(**kw) == code
+
+
+def test_prefill_cached_empty_is_a_noop():
+    assert _pfc(q=None, k=None, v=None, o=None, Nq=0) == 0
+
+
 def _dec(**kw):
     a = dict(q=P, k=P, v=P, lens=P, o=P, lse=None, B=2, Hq=8, Hkv=2, max_len=64, d=128,
              scale=0.1, dtype=esd.ATTN_BF16, ws=P, wsb=1 << 20)
@@ -151,11 +173,11 @@ def test_decode_empty_is_a_noop():
 
 def _decm(**kw):
     a = dict(q=P, k=P, v=P, lens=P, o=P, lse=None, B=2, Hq=8, Hkv=2, T=4, max_len=64, d=128,
-             scale=0.1, rope=0.0, dtype=esd.ATTN_BF16, ws=P, wsb=1 << 20)
+             scale=0.1, rope=0.0, dtype=esd.ATTN_BF16, odt=esd.ATTN_F32, ws=P, wsb=1 << 20)
     a.update(kw)
     return esd.lib().attn_decode_multi(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"], a["B"],
                                        a["Hq"], a["Hkv"], a["T"], a["max_len"], a["d"], a["scale"],
-                                       a["rope"], a["dtype"], a["ws"], a["wsb"], None)
+                                       a["rope"], a["dtype"], a["odt"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -163,6 +185,7 @@ def _decm(**kw):
     (dict(scale=0.0), 1), (dict(rope=-5.0), 1), (dict(rope=float("nan")), 1),
     (dict(dtype=esd.ATTN_F32), 2), (dict(d=96), 2), (dict(ws=None), 4), (dict(wsb=100), 4),
     (dict(ws=ctypes.c_void_p(272)), 1), (dict(B=1 << 12, Hq=1 << 12, Hkv=1, T=1 << 8), 2),
+    (dict(odt=5), 1), (dict(odt=-1), 1),
 ])
 def test_decode_multi_rejects_on_host(kw, code):
     assert _decm(**kw) == code
@@ -179,18 +202,19 @@ def test_decode_multi_workspace():
 
 def _decp(**kw):
     a = dict(q=P, k=P, v=P, table=P, lens=P, o=P, lse=None, B=2, Hq=8, Hkv=2, T=1, nblk=64,
-             bs=16, mb=8, d=128, scale=0.1, rope=0.0, dtype=esd.ATTN_BF16, ws=P, wsb=1 << 20)
+             bs=16, mb=8, d=128, scale=0.1, rope=0.0, dtype=esd.ATTN_BF16, odt=esd.ATTN_F32, ws=P,
+             wsb=1 << 20)
     a.update(kw)
     return esd.lib().attn_decode_paged(a["q"], a["k"], a["v"], a["table"], a["lens"], a["o"],
                                        a["lse"], a["B"], a["Hq"], a["Hkv"], a["T"], a["nblk"],
                                        a["bs"], a["mb"], a["d"], a["scale"], a["rope"], a["dtype"],
-                                       a["ws"], a["wsb"], None)
+                                       a["odt"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(table=None), 1), (dict(nblk=0), 1), (dict(mb=0), 1), (dict(bs=8), 2), (dict(bs=24), 2),
     (dict(bs=8192), 2), (dict(mb=1 << 20, bs=4096), 2), (dict(T=0), 1), (dict(lens=None), 1),
-    (dict(dtype=esd.ATTN_F32), 2), (dict(ws=None), 4), (dict(d=80), 2),
+    (dict(dtype=esd.ATTN_F32), 2), (dict(ws=None), 4), (dict(d=80), 2), (dict(odt=3), 1),
 ])
 def test_decode_paged_rejects_on_host(kw, code):
     assert _decp(**kw) == code

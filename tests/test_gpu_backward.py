@@ -8,7 +8,8 @@ relative to its largest magnitude, max|dX - ref| <= 2e-2 * max|ref| (about ten
 bf16 roundings), and by its root-mean-square error relative to the reference's,
 <= 1e-2 (both magnitudes floored at 1e-4, for gradients that are exactly 0).
 Small shapes are compared on every element; the full-size GQA case (B=2,
-Hq=32, Hkv=8, N=8192, d=128, RoPE) on sampled query and key rows.
+Hq=32, Hkv=8, N=8192, d=128, RoPE) on every (batch, KV head) pair at sampled
+query and key rows.
 """
 
 import math
@@ -149,9 +150,11 @@ def test_bwd_deterministic():
         assert np.array_equal(x, y)
 
 
-def test_bwd_gqa_n8192_sampled():
-    """Causal GQA + RoPE 1e4, B=2 Hq=32 Hkv=8 N=8192 d=128: dQ on sampled query
-    rows of the four heads of one KV head, dK and dV on sampled key rows."""
+def test_bwd_gqa_n8192_every_kv_head():
+    """Causal GQA + RoPE 1e4, B=2 Hq=32 Hkv=8 N=8192 d=128: for each of the 16
+    (batch, KV head) pairs, dQ on sampled query rows of its four query heads and
+    dK, dV on sampled key rows (edges of the 256-key and 64-query blocks the
+    kernels use, plus random rows drawn per pair)."""
     import torch
     w = W.WORKLOADS["gqa_rope_n8192"]
     q, k, v = W.fwd_inputs(w)
@@ -159,15 +162,18 @@ def test_bwd_gqa_n8192_sampled():
     say(f"bwd gqa_rope_n8192 shape: {w.note}")
     got = _run(q, k, v, do, True, w.scale, w.rope_base)
     N = w.Nq
-    rows = np.unique(np.concatenate([[0, 1, 31, 32, 63, 64, 127, 128, N // 2, N - 129, N - 33,
-                                      N - 32, N - 2, N - 1],
-                                     np.random.default_rng(11501).integers(0, N, 16)]))
-    b, g = 1, 5
-    sq, sk, sv = oa.attention_bwd_rows(q, k, v, do, b, g, rows, rows, causal=True, scale=w.scale,
-                                       rope_base=w.rope_base, dtype="bf16")
     G = w.Hq // w.Hkv
-    _grad_check(got[0][b, g * G:(g + 1) * G][:, rows], sq, f"bwd gqa_rope_n8192 dq ({len(rows)} rows x {G} heads)")
-    _grad_check(got[1][b, g, rows], sk, f"bwd gqa_rope_n8192 dk ({len(rows)} rows)")
-    _grad_check(got[2][b, g, rows], sv, f"bwd gqa_rope_n8192 dv ({len(rows)} rows)")
+    fixed = [0, 1, 31, 32, 63, 64, 127, 128, 255, 256, N // 2, N - 257, N - 256, N - 65, N - 64,
+             N - 33, N - 32, N - 2, N - 1]
+    rng = np.random.default_rng(11501)
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            rows = np.unique(np.concatenate([fixed, rng.integers(0, N, 12)]))
+            sq, sk, sv = oa.attention_bwd_rows(q, k, v, do, b, g, rows, rows, causal=True,
+                                               scale=w.scale, rope_base=w.rope_base, dtype="bf16")
+            tag = f"bwd gqa_rope_n8192 b={b} g={g}"
+            _grad_check(got[0][b, g * G:(g + 1) * G][:, rows], sq, f"{tag} dq ({len(rows)} rows x {G} heads)")
+            _grad_check(got[1][b, g, rows], sk, f"{tag} dk ({len(rows)} rows)")
+            _grad_check(got[2][b, g, rows], sv, f"{tag} dv ({len(rows)} rows)")
     del got
     torch.cuda.empty_cache()

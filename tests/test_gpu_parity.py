@@ -2,9 +2,9 @@
 
 Tolerances: bf16 inputs max|dO| <= 1e-2 and max|dlse| <= 1e-3; fp32 inputs
 1e-4 on both.  Small shapes are compared element by element; the full-size
-workloads are compared on every output where the oracle is cheap (the fp32
-single-head case, the MHA causal case, decode) and on sampled rows elsewhere,
-in the same launch configuration the benchmark times.
+workloads in the launch configuration the benchmark times: every output of the
+fp32 single-head case, the MHA causal case, the causal GQA N=8192 case and
+decode; all 64 heads of the N=32768 case at the edges of sampled row blocks.
 """
 
 import math
@@ -167,31 +167,67 @@ def test_mha_d64_n2048_full():
     check(o, lse, ro, rl, "bf16", "mha_d64_n2048 all outputs")
 
 
-def _sampled(w, heads, n_random, seed):
+def test_gqa_rope_n8192_every_row():
+    """Causal GQA + RoPE 1e4, B=2 Hq=32 Hkv=8 N=8192 d=128, in the launch
+    configuration the benchmark times: every (batch, head) and every row
+    against the oracle."""
+    w = W.WORKLOADS["gqa_rope_n8192"]
     q, k, v = W.fwd_inputs(w)
     say(f"{w.name}: {w.note}")
     o, lse = _run_fwd(q, k, v, w.dtype, w.causal, w.scale, w.rope_base)
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
-    N = w.Nq
-    rng = np.random.default_rng(seed)
-    fixed = [0, 1, 2, 31, 32, 63, 64, 65, 127, 128, 255, 256, N // 2, N - 129, N - 128, N - 65,
-             N - 64, N - 2, N - 1]
+    rows = np.arange(w.Nq)
     kc = {}
-    for (b, h) in heads:
-        rows = np.unique(np.concatenate([fixed, rng.integers(0, N, n_random)]))
-        ro, rl = oa.attention_rows(q, k, v, b, h, rows, causal=w.causal, scale=w.scale,
-                                   rope_base=w.rope_base, dtype=w.dtype, _kcache=kc)
-        check(o[b, h, rows], lse[b, h, rows], ro, rl, w.dtype, f"{w.name} b={b} h={h} ({len(rows)} rows)")
+    eo = el = 0.0
+    for b in range(w.B):
+        for h in range(w.Hq):
+            ro, rl = oa.attention_rows(q, k, v, b, h, rows, causal=True, scale=w.scale,
+                                       rope_base=w.rope_base, dtype=w.dtype, _kcache=kc)
+            assert np.all(np.isfinite(o[b, h])) and np.all(np.isfinite(lse[b, h]))
+            eo = max(eo, max_err(o[b, h], ro))
+            el = max(el, max_err(lse[b, h], rl))
+        say(f"{w.name}: batch {b} done, max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    assert eo <= 1e-2 and el <= 1e-3, (eo, el)
 
 
-def test_gqa_rope_n8192_sampled():
-    w = W.WORKLOADS["gqa_rope_n8192"]
-    _sampled(w, [(0, 0), (0, 3), (0, 4), (1, 17), (1, 31)], 48, 3)
+def _block_edge_rows(N, rows_per_block, rng, n_blocks, n_random):
+    """Rows at both edges of sampled workgroup row blocks and of the 32-row
+    wave blocks inside them, plus random rows; the first and last blocks are
+    always sampled."""
+    nrb = (N + rows_per_block - 1) // rows_per_block
+    blocks = np.unique(np.concatenate([[0, 1, nrb // 2, nrb - 2, nrb - 1],
+                                       rng.integers(0, nrb, n_blocks)]))
+    rows = []
+    for blk in blocks:
+        r0 = blk * rows_per_block
+        for off in range(0, rows_per_block, 32):
+            rows += [r0 + off, r0 + off + 31]
+    rows = np.asarray(rows)
+    rows = np.concatenate([rows[rows < N], rng.integers(0, N, n_random)])
+    return np.unique(rows)
 
 
-def test_gqa_rope_n32768_sampled():
+def test_gqa_rope_n32768_all_heads_block_edges():
+    """Long-context GQA + RoPE 5e5, B=1 Hq=64 Hkv=8 N=32768 d=128, Q,K ~ N(0,16):
+    all 64 heads, each on at least 128 rows at both edges of 96-row workgroup
+    blocks (4 heads x 3 waves of 32 rows share a KV head's tiles) and of the
+    wave blocks inside them, at blocks sampled per head."""
     w = W.WORKLOADS["gqa_rope_n32768"]
-    _sampled(w, [(0, 0), (0, 7), (0, 8), (0, 63)], 48, 5)
+    q, k, v = W.fwd_inputs(w)
+    say(f"{w.name}: {w.note}")
+    o, lse = _run_fwd(q, k, v, w.dtype, w.causal, w.scale, w.rope_base)
+    rng = np.random.default_rng(5)
+    kc = {}
+    eo = el = 0.0
+    for h in range(w.Hq):
+        rows = _block_edge_rows(w.Nq, 96, rng, 20, 12)
+        assert len(rows) >= 128, len(rows)
+        ro, rl = oa.attention_rows(q, k, v, 0, h, rows, causal=True, scale=w.scale,
+                                   rope_base=w.rope_base, dtype=w.dtype, _kcache=kc)
+        assert np.all(np.isfinite(o[0, h, rows])) and np.all(np.isfinite(lse[0, h, rows]))
+        eo = max(eo, max_err(o[0, h, rows], ro))
+        el = max(el, max_err(lse[0, h, rows], rl))
+    say(f"{w.name}: 64 heads, max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    assert eo <= 1e-2 and el <= 1e-3, (eo, el)
 
 
 def test_decode_b32_full():
