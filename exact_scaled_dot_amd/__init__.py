@@ -62,7 +62,13 @@ def lib():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(
             f"{LIB_PATH} is missing: build it with `python -m exact_scaled_dot_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+    _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def _declare(L):
+    """Set the argument and result types of every entry point on a loaded
+    library object (the C declarations of include/attn.h)."""
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.attn_status_str.argtypes = [i]
     L.attn_status_str.restype = ctypes.c_char_p
@@ -97,7 +103,6 @@ def lib():
     L.attn_decode_noalloc.restype = i
     L.attn_rope_apply.argtypes = [vp, vp, i, i, i, i, i, f, i, vp]
     L.attn_rope_apply.restype = i
-    _lib = L
     return L
 
 

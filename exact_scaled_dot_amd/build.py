@@ -20,8 +20,8 @@ OUT = os.path.join(HERE, "libattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["attn_host.cpp", "rope.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip",
-           "backward.hip"]
+SOURCES = ["attn_host.cpp", "rope_table.cpp", "rope.hip", "prefill_bf16.hip", "prefill_f32.hip",
+           "decode.hip", "backward.hip"]
 
 # Per-source extra flags.  The bf16 kernels never see NaN (inputs are finite by
 # contract; masking uses -inf), so max chains need no NaN canonicalisation and

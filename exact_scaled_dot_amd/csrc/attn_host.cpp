@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 
@@ -79,6 +80,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
         return fail(ATTN_ERR_INVALID, "rope_base must be 0 or a finite positive base");
     if (rope_base != 0.f && Nq > Nk)
         return fail(ATTN_ERR_INVALID, "RoPE needs Nq <= Nk (query positions Nk-Nq+i must be >= 0)");
+    if (rope_base != 0.f && Nk > attn::kMaxRopePositions)
+        return fail(ATTN_ERR_UNSUPPORTED, "RoPE positions must be below 2^22");
     if (!known_dtype(dtype)) return fail(ATTN_ERR_INVALID, "unknown dtype");
     if (!known_dtype(o_dtype)) return fail(ATTN_ERR_INVALID, "unknown output dtype");
     if (!supported_d(d)) return fail(ATTN_ERR_UNSUPPORTED, "head dim must be 64 or 128");
@@ -105,8 +108,9 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
         int dev = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e != hipSuccess) return fail(ATTN_ERR_HIP, "hipGetDevice");
-        const double2* tab = attn::rope_table(dev, rope_base, d, Nk, &e);
-        if (!tab) return fail(ATTN_ERR_HIP, "RoPE table");
+        const double2* tab = nullptr;
+        const int rc = attn::rope_table(dev, rope_base, d, Nk, stream, &tab);
+        if (rc != ATTN_OK) return fail(rc, "RoPE table (not built while a stream is captured)");
         if (rotate_k) {
             // K rotated once into the workspace; Q is rotated as it is loaded.
             const long long rows = (long long)B * Hkv * Nk;
@@ -209,6 +213,8 @@ int decode_impl(const void* q, const void* k, const void* v, const int32_t* tabl
         return fail(ATTN_ERR_UNSUPPORTED, "one sequence's cache must be under 2 GiB (32-bit buffer offsets)");
     if ((long long)B * Hq * T > 0x7fffffffLL)
         return fail(ATTN_ERR_UNSUPPORTED, "B * Hq * T must fit in 31 bits");
+    if (rope_base > 0.f && max_len > attn::kMaxRopePositions)
+        return fail(ATTN_ERR_UNSUPPORTED, "RoPE positions must be below 2^22");
     if (B == 0 || Hq == 0) return ATTN_OK;
     if (!q || !k || !v || !seq_lens || !o) return fail(ATTN_ERR_INVALID, "null pointer");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
@@ -247,8 +253,8 @@ int decode_impl(const void* q, const void* k, const void* v, const int32_t* tabl
         int dev = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e != hipSuccess) return fail(ATTN_ERR_HIP, "hipGetDevice");
-        a.rope_tab = attn::rope_table(dev, rope_base, d, max_len, &e);
-        if (!a.rope_tab) return fail(ATTN_ERR_HIP, "RoPE table");
+        const int rc = attn::rope_table(dev, rope_base, d, max_len, stream, &a.rope_tab);
+        if (rc != ATTN_OK) return fail(rc, "RoPE table (not built while a stream is captured)");
     }
     a.chunk = chunk;
     a.nchunks = (max_len + chunk - 1) / chunk;
@@ -345,6 +351,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* o, const 
     if (!supported_d(d)) return fail(ATTN_ERR_UNSUPPORTED, "head dim must be 64 or 128");
     if ((long long)Nk * d * 4 >= (1LL << 31) || (long long)Nq * d * 4 >= (1LL << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "one head's Q, K or V must be under 2 GiB (32-bit buffer offsets)");
+    if (rope_base != 0.f && Nk > attn::kMaxRopePositions)
+        return fail(ATTN_ERR_UNSUPPORTED, "RoPE positions must be below 2^22");
     if (B == 0 || Hq == 0 || Nq == 0) return ATTN_OK;
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
         return fail(ATTN_ERR_INVALID, "null pointer");
@@ -378,8 +386,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* o, const 
         int dev = 0;
         e = hipGetDevice(&dev);
         if (e != hipSuccess) return fail(ATTN_ERR_HIP, "hipGetDevice");
-        tab = attn::rope_table(dev, rope_base, d, Nk, &e);
-        if (!tab) return fail(ATTN_ERR_HIP, "RoPE table");
+        const int rc = attn::rope_table(dev, rope_base, d, Nk, stream, &tab);
+        if (rc != ATTN_OK) return fail(rc, "RoPE table (not built while a stream is captured)");
         uint16_t* qr = reinterpret_cast<uint16_t*>(w);
         w += align256(rows * d * 2);
         uint16_t* kr = reinterpret_cast<uint16_t*>(w);
@@ -408,15 +416,17 @@ int attn_rope_apply(const void* x, void* out, int B, int H, int N, int d,
     if (!known_dtype(dtype)) return fail(ATTN_ERR_INVALID, "unknown dtype");
     if (d % (dtype == ATTN_BF16 ? 8 : 4) != 0 || d > 512)
         return fail(ATTN_ERR_UNSUPPORTED, "head dim must be a multiple of 8 (bf16) / 4 (f32), <= 512");
-    if ((long long)pos_offset + N > 0x40000000LL) return fail(ATTN_ERR_INVALID, "positions too large");
+    if ((long long)pos_offset + N > attn::kMaxRopePositions)
+        return fail(ATTN_ERR_UNSUPPORTED, "RoPE positions must be below 2^22");
     if (B == 0 || H == 0 || N == 0) return ATTN_OK;
     if (!x || !out) return fail(ATTN_ERR_INVALID, "null pointer");
     if (!aligned16(x) || !aligned16(out)) return fail(ATTN_ERR_INVALID, "x and out must be 16-byte aligned");
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "hipGetDevice");
-    const double2* tab = attn::rope_table(dev, rope_base, d, pos_offset + N, &e);
-    if (!tab) return fail(ATTN_ERR_HIP, "RoPE table");
+    const double2* tab = nullptr;
+    const int rc = attn::rope_table(dev, rope_base, d, pos_offset + N, stream, &tab);
+    if (rc != ATTN_OK) return fail(rc, "RoPE table (not built while a stream is captured)");
     const long long rows = (long long)B * H * N;
     if (dtype == ATTN_BF16)
         e = attn::launch_rope_bf16(static_cast<const uint16_t*>(x), static_cast<uint16_t*>(out), rows, N, d,

@@ -95,8 +95,14 @@ struct BwdArgs {
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 
-// Device table of (cos, sin) in fp64, [npos][d/2]; created or grown on demand.
-// Returns null on failure (HIP error stored in *err).
-const double2* rope_table(int device, float base, int d, int npos, hipError_t* err);
+// Largest number of RoPE positions (0 .. kMaxRopePositions - 1) any call may
+// use: every K row range the forward accepts at d = 128 (Nk * d * 4 < 2^31).
+constexpr int kMaxRopePositions = 1 << 22;
+
+// Device table of (cos, sin) in fp64, [npos][d/2], covering positions
+// 0 .. npos - 1 (or more); created or grown on demand (rope_table.cpp).
+// Returns an attn_status; *tab is set on ATTN_OK.  Building refuses to run
+// while `stream` is being captured (ATTN_ERR_HIP).
+int rope_table(int device, float base, int d, int npos, hipStream_t stream, const double2** tab);
 
 }  // namespace attn

@@ -35,9 +35,20 @@
  * before the product, so the result is the attention of the rounded rotated
  * operands.
  *
+ * RoPE positions must be below 2^22 (4,194,304; larger ones return
+ * ATTN_ERR_UNSUPPORTED): every K row range attn_fwd accepts at d = 128.
+ *
  * Ownership: the caller owns every buffer, including workspaces.  The library
- * keeps one device table of fp64 cos/sin per (device, rope_base, d), created on
- * the first RoPE call that needs it (a blocking upload) and kept until exit.
+ * keeps one device table of fp64 cos/sin per (device, rope_base, d) covering
+ * positions 0 .. P - 1, P the largest position count asked for so far rounded
+ * up to a power of two (at least 1024; P * d / 2 * 16 bytes, at most 4 GiB at
+ * d = 128).  It is built on the first RoPE call that needs it, or a longer
+ * one: the host evaluates it with the C library in pieces of at most 16 MB and
+ * uploads them with blocking copies (hipMalloc, hipMemcpy).  Such a call made
+ * while its stream is being captured into a graph returns ATTN_ERR_HIP before
+ * any allocation, so code that captures makes one RoPE call of the longest
+ * length beforehand.  Older tables stay allocated until exit (kernels queued
+ * earlier may still read them).
  * Entry points are thread-safe; calls that share a workspace must be ordered by
  * the caller (same stream or events).
  */
@@ -303,7 +314,8 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
  * RoPE on its own: out[b,h,n,:] = rotate(x[b,h,n,:], position pos_offset + n),
  * rounded to `dtype` exactly as attn_fwd rounds the rotated operands.
  * x, out  device [B, H, N, d] of `dtype` (may alias).  d a multiple of 8
- *         (bf16) or 4 (fp32), at most 512.
+ *         (bf16) or 4 (fp32), at most 512.  pos_offset + N <= 2^22, else
+ *         ATTN_ERR_UNSUPPORTED.
  */
 int attn_rope_apply(const void* x, void* out, int B, int H, int N, int d,
                     int pos_offset, float rope_base, attn_dtype dtype,

@@ -276,3 +276,13 @@ def test_rope_apply_rejects_on_host():
     assert L.attn_rope_apply(P, P, 1, 1, 4, 16, 0, 0.0, esd.ATTN_BF16, None) == 1
     assert L.attn_rope_apply(None, P, 1, 1, 4, 16, 0, 100.0, esd.ATTN_BF16, None) == 1
     assert L.attn_rope_apply(None, None, 0, 1, 4, 16, 0, 100.0, esd.ATTN_BF16, None) == 0
+    # positions past 2^22 (the RoPE table's limit) are refused before any HIP call
+    assert L.attn_rope_apply(P, P, 1, 1, 4, 16, (1 << 22) - 3, 100.0, esd.ATTN_BF16, None) == 2
+    assert L.attn_rope_apply(P, P, 1, 1, 4, 16, 1 << 30, 100.0, esd.ATTN_BF16, None) == 2
+
+
+def test_rope_positions_past_the_table_limit_rejected():
+    # d = 64 allows 5M keys per head, but RoPE positions stop at 2^22
+    assert _fwd(Nq=8, Nk=5 << 20, rope=100.0, ws=P, wsb=1 << 40) == 2
+    assert _decm(max_len=5 << 20, d=64, rope=100.0) == 2
+    assert _pfc(Nq=8, Nk=5 << 20, rope=100.0) == 2

@@ -121,3 +121,38 @@ def test_concurrent_calls_from_threads():
         torch.cuda.synchronize()
         assert np.array_equal(results[i][0], host(o)) and np.array_equal(results[i][1], host(l))
     say("concurrent calls from 4 threads: identical to serial calls")
+
+
+def test_rope_table_not_built_inside_a_capture():
+    """A RoPE call whose table does not exist yet, made while its stream is being
+    captured, returns an error (the table would need blocking copies) and leaves
+    the capture intact: the rest of the graph replays like the eager calls."""
+    import torch
+    B, Hq, Hkv, N, d = 1, 4, 2, 150, 128
+    q = dev(W.normal((B, Hq, N, d), 13301, 1.0, "bf16"))
+    k = dev(W.normal((B, Hkv, N, d), 13302, 1.0, "bf16"))
+    v = dev(W.normal((B, Hkv, N, d), 13303, 1.0, "bf16"))
+    o = torch.empty((B, Hq, N, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device="cuda")
+    o2 = torch.empty_like(o)
+    ws = torch.empty(esd.fwd_workspace_bytes(B, Hkv, N, d, 9876.5, esd.ATTN_BF16),
+                     dtype=torch.uint8, device="cuda")
+    esd.fwd(q, k, v, True, 1 / math.sqrt(d), 0.0, out=o, lse=lse)
+    torch.cuda.synchronize()
+    ref = (host(o).copy(), host(lse).copy())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        with pytest.raises(esd.AttnError):
+            # base 9876.5 has no table yet
+            esd.fwd(q, k, v, True, 1 / math.sqrt(d), 9876.5, out=o2, workspace=ws)
+        esd.fwd(q, k, v, True, 1 / math.sqrt(d), 0.0, out=o, lse=lse)
+    o.fill_(float("nan"))
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert np.array_equal(host(o), ref[0]) and np.array_equal(host(lse), ref[1])
+    # outside the capture the same call builds the table and runs
+    esd.fwd(q, k, v, True, 1 / math.sqrt(d), 9876.5, out=o2, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(host(o2)))
+    say("RoPE table refused inside a capture; the graph replays; built afterwards")
