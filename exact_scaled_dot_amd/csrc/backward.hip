@@ -13,10 +13,11 @@
 // Three kernels:
 //   * prep: per query row, dO rounded to bf16 for the matrix cores, D = dO . O
 //     (fp32) from that rounded dO, lse converted to the log2 domain.
-//   * dK/dV: a workgroup owns 256 keys of one KV head (8 waves x 32 keys, K
-//     and V of a wave held in registers as MFMA operands) and streams 64-query
-//     tiles of Q and dO of every query head that reads this KV head through
-//     LDS, so the GQA sum over heads happens in the accumulators.  Each tile
+//   * dK/dV: a workgroup owns 256 keys of one KV head (8 waves x 32 keys; K of
+//     a wave held in registers and V in the wave's slice of LDS as MFMA
+//     operands, which keeps the wave within 256 registers) and streams
+//     64-query tiles of Q and dO of every query head that reads this KV head
+//     through LDS, so the GQA sum over heads happens in the accumulators.  Each tile
 //     takes two updates of 32 queries between barriers, so the two waves of a
 //     SIMD drift out of phase within a tile; a wave skips an update whose rows
 //     see none of its keys (causal).  Per update and wave: S = Q K^T and
@@ -29,10 +30,14 @@
 // Both stream their tiles through two LDS buffers with one barrier per tile:
 // the next tile is loaded while the current one is computed (dK/dV straight
 // into LDS, dQ through registers).
-// A tile that is read both by rows (16 bytes per lane, 16 lanes per LDS cycle:
-// the row stride must be an odd multiple of 4 banks) and transposed (four
-// rows' 64-byte pieces per cycle: an odd multiple of 16 banks) is stored
-// twice, once padded for each, which costs one more LDS write per chunk.
+// A tile is read both by rows (16 bytes per lane; 16 lanes per LDS cycle take
+// 16 consecutive rows, conflict-free when the row stride is 4 banks mod 64) and
+// transposed (a 16-lane group takes 32 bytes of each of four rows, the rows of
+// one k-slot group).  The pairing of score rows with tile rows is free as long
+// as both operands of a product use the same one, so within each 16-row block
+// score row 4a + e is taken from tile row 4e + a (perm16): the four rows of a
+// k-slot group are then 4 rows apart, 16 banks apart at that stride, and both
+// kinds of read are conflict-free on one copy of the tile.
 
 #include "device_common.h"
 #include "launch.h"
@@ -44,24 +49,30 @@ namespace {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRP = 8;       // row pad (elements) of tiles read by rows: stride = 4 banks mod 64
-constexpr int kTP = 32;      // row pad of tiles read transposed: stride = 16 banks mod 64
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
-// Transposed 32x16 operand fragment from a row-major LDS tile: lane l gets
-// column c0 + l % 32 of the 8 rows r0 + 4h + {0..3}, r0 + 8 + 4h + {0..3}
-// (h = l / 32), the k-slot order in which score accumulators hand over rows.
+// Tile row of score row s: within each 16-row block, 4a + e -> 4e + a.
+__device__ __forceinline__ int perm16(int s) {
+    return (s & ~15) | ((s & 3) << 2) | ((s >> 2) & 3);
+}
+
+// Transposed 32x16 operand fragment from a row-major LDS tile whose rows are
+// paired with score rows by perm16: lane l gets column c0 + l % 32 of the
+// score rows r0 + 4h + {0..3}, r0 + 8 + 4h + {0..3} (h = l / 32), the k-slot
+// order in which score accumulators hand over rows, i.e. of the tile rows
+// r0 + h + {0, 4, 8, 12} and r0 + 2 + h + {0, 4, 8, 12}.
 __device__ __forceinline__ bf16x8 tr_fragment(const uint16_t* tile, int stride, int r0, int c0,
                                               int lane) {
     const int grp = lane >> 4;
     const int w16 = lane & 15;
-    const int row = r0 + 4 * (grp >> 1) + (w16 >> 2);
+    const int row = r0 + 4 * (w16 >> 2) + (grp >> 1);
     const int col = c0 + 16 * (grp & 1) + 4 * (w16 & 3);
     const s16x4 lo = lds_read_tr(tile + row * stride + col);
-    const s16x4 hi = lds_read_tr(tile + (row + 8) * stride + col);
+    const s16x4 hi = lds_read_tr(tile + (row + 2) * stride + col);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -112,20 +123,15 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 float* __restrict__ dk, float* __restrict__ dv, int B, int Hq, int Hkv, int Nq,
                 int Nk, float scale_log2, float scale, const double2* __restrict__ tab) {
     constexpr int CPR = D / 8;   // 16-byte chunks per row
-    constexpr int RS = D + kRP;  // stride of the row-read copies
-    constexpr int TS = D + kTP;  // stride of the transposed-read copies
+    constexpr int RS = D + kRP;  // tile row stride: 4 banks mod 64
     // Tiles go from memory straight into LDS (buffer_load ... lds, 1 KB per
-    // instruction), so each copy is a separate object sized to whole
+    // instruction), so each tile is a separate object sized to whole
     // instructions: the compiler then knows the loads into one buffer do not
     // alias the reads from the other.
     constexpr int RSZ = (kQT * RS + 511) / 512 * 512;
-    constexpr int TSZ = (kQT * TS + 511) / 512 * 512;
     __shared__ __attribute__((aligned(16))) uint16_t Qr0[RSZ], Qr1[RSZ], Or0[RSZ], Or1[RSZ];
-    __shared__ __attribute__((aligned(16))) uint16_t Qt0[TSZ], Qt1[TSZ], Ot0[TSZ], Ot1[TSZ];
     auto Qr = [&](int P) -> uint16_t* { return P ? Qr1 : Qr0; };
     auto Or = [&](int P) -> uint16_t* { return P ? Or1 : Or0; };
-    auto Qt = [&](int P) -> uint16_t* { return P ? Qt1 : Qt0; };
-    auto Ot = [&](int P) -> uint16_t* { return P ? Ot1 : Ot0; };
     __shared__ __attribute__((aligned(16))) float Ls[2][kQT];
     __shared__ __attribute__((aligned(16))) float Dsh[2][kQT];
 
@@ -151,12 +157,17 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const_cast<uint16_t*>(k + kvoff), (short)0, Nk * D * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(v + kvoff), (short)0, Nk * D * 2, 0x00020000);
-    bf16x8 kf[D / 16], vf[D / 16];
+    // K of this wave's keys in registers; V in this wave's slice of LDS (row
+    // stride 4 banks mod 64), read as the B operand of dP = dO V^T
+    bf16x8 kf[D / 16];
+    __shared__ __attribute__((aligned(16))) uint16_t Vw[kKW][kKeysW * RS];
+    uint16_t* vw = Vw[wave];
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
         const int boff = ((kw0 + l32) * D + 16 * s + 8 * half) * 2;
         kf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, boff, 0, 0));
-        vf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, boff, 0, 0));
+        *reinterpret_cast<u32x4*>(vw + l32 * RS + 16 * s + 8 * half) =
+            __builtin_amdgcn_raw_buffer_load_b128(rv, boff, 0, 0);
     }
     f32x16 dka[D / 32], dva[D / 32];
 #pragma unroll
@@ -186,7 +197,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const int spr = stride / 8;
         const int ninst = (kQT * spr + 63) / 64;
 #pragma unroll
-        for (int i = 0; i < (kQT * (D + kTP) / 8 / 64 + kKW) / kKW; ++i) {
+        for (int i = 0; i < (kQT * RS / 8 / 64 + kKW) / kKW; ++i) {
             const int j = min(wave + kKW * i, ninst - 1);  // wave-uniform
             const int slot = 64 * j + lane;
             const int rr = slot / spr;
@@ -209,17 +220,16 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             const_cast<uint16_t*>(do16 + qoff * D), (short)0, Nq * D * 2, 0x00020000);
         dma(rq, Qr(P), RS, q0);
         dma(ro, Or(P), RS, q0);
-        dma(rq, Qt(P), TS, q0);
-        dma(ro, Ot(P), TS, q0);
-        // every thread fetches the statistics of row tid % 64 (the same value
-        // for the same slot, so the stores need no branch).  Buffer loads
-        // bounded to this head's rows: rows past Nq read 0, and their lse
-        // becomes +inf (P = 2^-inf = 0) by an add, not a select of a load
+        // every thread fetches the statistics of score row tid % 64, i.e. of
+        // tile row perm16(tid % 64) (the same value for the same slot, so the
+        // stores need no branch).  Buffer loads bounded to this head's rows:
+        // rows past Nq read 0, and their lse becomes +inf (P = 2^-inf = 0) by
+        // an add, not a select of a load
         const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<float*>(lse2 + qoff), (short)0, Nq * 4, 0x00020000);
         const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<float*>(dvec + qoff), (short)0, Nq * 4, 0x00020000);
-        const int qr = q0 + lane;
+        const int qr = q0 + perm16(lane);
         r.l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, qr * 4, 0, 0)) +
               (qr < Nq ? 0.f : INFINITY);
         r.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, qr * 4, 0, 0));
@@ -229,7 +239,9 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         Dsh[buf][lane] = r.d;
     };
     // S = Q K^T and dP = dO V^T of one tile: lane holds key column l32 and
-    // query rows 8*(i/4) + 4*half + i%4
+    // score rows 8*(i/4) + 4*half + i%4, i.e. the queries of tile rows perm16
+    // of those
+    const int prow = perm16(l32);  // tile row of this lane's A operand
     auto scores = [&](int buf, int sub, f32x16& sa, f32x16& pa) {
         sa = f32x16{};
         pa = f32x16{};
@@ -237,10 +249,11 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const uint16_t* Ob = Or(buf) + kQS * RS * sub;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-            const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&Qb[l32 * RS + 16 * s + 8 * half]);
+            const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&Qb[prow * RS + 16 * s + 8 * half]);
             sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[s], sa, 0, 0, 0);
-            const bf16x8 ao = *reinterpret_cast<const bf16x8*>(&Ob[l32 * RS + 16 * s + 8 * half]);
-            pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[s], pa, 0, 0, 0);
+            const bf16x8 ao = *reinterpret_cast<const bf16x8*>(&Ob[prow * RS + 16 * s + 8 * half]);
+            const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&vw[l32 * RS + 16 * s + 8 * half]);
+            pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, bv, pa, 0, 0, 0);
         }
     };
     // P and dS of one tile, then dV += P^T dO and dK += dS^T Q over its 32
@@ -255,7 +268,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 4 * j + e;
-                const int qi = q0 + 8 * j + 4 * half + e;
+                const int qi = q0 + perm16(8 * j + 4 * half + e);
                 // branch-free: a hidden pair gets 2^-inf = 0
                 const float x = fmaf(sa[i], scale_log2, -l4[e]);
                 p[e] = fast_exp2(qi >= qmin ? x : -INFINITY);
@@ -266,8 +279,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             dw[j >> 1][2 * (j & 1)] = pack_bf16x2(ds[0], ds[1]);
             dw[j >> 1][2 * (j & 1) + 1] = pack_bf16x2(ds[2], ds[3]);
         }
-        const uint16_t* Qb = Qt(buf);
-        const uint16_t* Ob = Ot(buf);
+        const uint16_t* Qb = Qr(buf);
+        const uint16_t* Ob = Or(buf);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const u32x4 p4 = {pw[ks][0], pw[ks][1], pw[ks][2], pw[ks][3]};
@@ -276,9 +289,9 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             const bf16x8 dA = __builtin_bit_cast(bf16x8, d4);
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-                const bf16x8 bo = tr_fragment(Ob, TS, kQS * sub + 16 * ks, 32 * db, lane);
+                const bf16x8 bo = tr_fragment(Ob, RS, kQS * sub + 16 * ks, 32 * db, lane);
                 dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pA, bo, dva[db], 0, 0, 0);
-                const bf16x8 bq = tr_fragment(Qb, TS, kQS * sub + 16 * ks, 32 * db, lane);
+                const bf16x8 bq = tr_fragment(Qb, RS, kQS * sub + 16 * ks, 32 * db, lane);
                 dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dA, bq, dka[db], 0, 0, 0);
             }
         }
@@ -299,6 +312,9 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const int q0 = tile_q0(it);
 #pragma unroll
         for (int u = 0; u < kQT / kQS; ++u) {
+            // one update at a time: overlapped by the scheduler, two updates
+            // no longer fit the registers
+            __builtin_amdgcn_sched_barrier(0);
             // skip an update none of whose rows sees a key of this wave
             if (!CAUSAL || q0 + kQS * u + kQS - 1 >= kw0 - off) {
                 f32x16 sc, pc;
@@ -364,9 +380,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     constexpr int LPT = kBc * CPR / NT;
     static_assert(LPT >= 1 && (kBc * CPR) % NT == 0, "tile/thread mismatch");
     constexpr int RS = D + kRP;
-    constexpr int TS = D + kTP;
     __shared__ __attribute__((aligned(16))) uint16_t Kr[2][kBc * RS];
-    __shared__ __attribute__((aligned(16))) uint16_t Kt[2][kBc * TS];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBc * VS];
 
     const int tid = threadIdx.x;
@@ -447,7 +461,6 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             const int r = c / CPR;
             const int col = (c - r * CPR) * 8;
             *reinterpret_cast<u32x4*>(&Kr[buf][r * RS + col]) = pk[i];
-            *reinterpret_cast<u32x4*>(&Kt[buf][r * TS + col]) = pk[i];
             *reinterpret_cast<u32x4*>(&Vs[buf][r * VS + col]) = pv[i];
         }
     };
@@ -459,19 +472,20 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const int buf = t & 1;
         if (t + 1 < ntiles) gload(key0 + kBc);
         const uint16_t* Krb = Kr[buf];
-        const uint16_t* Ktb = Kt[buf];
         const uint16_t* Vt = Vs[buf];
+        const int prow = perm16(l32);  // tile row (key) of this lane's A operands
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             if (CAUSAL && key0 + 32 * kb > wave_klast) break;  // wave-uniform
             // S^T = K Q^T and dP^T = V dO^T for 32 keys: lane holds query l32,
-            // keys key0 + 32kb + 8*(i/4) + 4*half + i%4
+            // score rows 8*(i/4) + 4*half + i%4, i.e. the keys of tile rows
+            // key0 + 32kb + perm16 of those
             f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
             for (int s = 0; s < D / 16; ++s) {
-                const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&Krb[(kb * 32 + l32) * RS + 16 * s + 8 * half]);
+                const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&Krb[(kb * 32 + prow) * RS + 16 * s + 8 * half]);
                 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[s], sacc, 0, 0, 0);
-                const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Vt[(kb * 32 + l32) * VS + 16 * s + 8 * half]);
+                const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Vt[(kb * 32 + prow) * VS + 16 * s + 8 * half]);
                 pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[s], pacc, 0, 0, 0);
             }
             uint32_t da[2][4];
@@ -481,7 +495,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = 4 * j + e;
-                    const int kk = key0 + kb * 32 + 8 * j + 4 * half + e;
+                    const int kk = key0 + kb * 32 + perm16(8 * j + 4 * half + e);
                     // branch-free: a hidden pair gets 2^-inf = 0
                     const float x = fmaf(sacc[i], scale_log2, -lrow);
                     const float p = fast_exp2(kk <= klast ? x : -INFINITY);
@@ -497,7 +511,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const bf16x8 dB = __builtin_bit_cast(bf16x8, d4);
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const bf16x8 ak = tr_fragment(Ktb, TS, kb * 32 + 16 * ks, 32 * db, lane);
+                    const bf16x8 ak = tr_fragment(Krb, RS, kb * 32 + 16 * ks, 32 * db, lane);
                     acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, dB, acc[db], 0, 0, 0);
                 }
             }
