@@ -11,13 +11,20 @@
 // comparison table in "Transformer Architecture Breakdown", section 4.3 names.
 //
 // gfx950 mapping
-//   * workgroup = 12 waves at d = 128, three per SIMD (8 at d = 64); each wave
-//     owns 32 query rows of one query head.  The waves of a workgroup cover query heads of one KV
-//     head (GQA group) and share every K/V tile, so a tile is read from memory
-//     once per group of heads.  Each wave runs a plain sequence per 32 keys
-//     (scores, mask, max, rescale, weights, P V); with three waves on a SIMD the
-//     hardware overlaps one wave's matrix products with another's vector work,
-//     and 168 registers per wave leave room for exactly three.
+//   * workgroup = 8 waves, two per SIMD; at d = 128 each wave owns 64 query
+//     rows of one query head as two 32-row blocks (at d = 64, one block of 32).
+//     Every K and V operand a wave reads from LDS feeds the products of both
+//     blocks, and the 512 query rows of a workgroup share each K/V tile: half
+//     the LDS operand reads and three quarters of the tile loads per product of
+//     one 32-row block per wave with three waves per SIMD.  The waves of a
+//     workgroup cover query heads of one KV head (GQA group), so a tile is read
+//     from memory once per group of heads.  The O accumulators of both blocks
+//     and the Q operands of the first stay in registers; the second block's Q
+//     rows sit in the wave's slice of LDS (256 registers per wave would not
+//     hold both).  Each wave runs a plain sequence per 32 keys (scores, mask,
+//     max, rescale, weights, P V for both blocks); the two blocks' independent
+//     chains and the other wave of the SIMD give the overlap of matrix and
+//     vector work.
 //   * K/V tiles of 64 keys are double-buffered in LDS.  The tiles arrive
 //     straight from memory (buffer_load ... lds) while the previous tile is
 //     used, with one barrier per tile; each tile takes two online-softmax
@@ -55,11 +62,14 @@ namespace {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// waves per workgroup: three per SIMD at d = 128 (168 registers each); at
-// d = 64 two per SIMD, so that a workgroup of one query head covers 256 rows
-// and short sequences still give many workgroups
+// waves per workgroup: two per SIMD (256 registers each at d = 128)
 template <int D>
-constexpr int waves_for() { return D == 128 ? 12 : 8; }
+constexpr int waves_for() { return 8; }
+// 32-row query blocks per wave: two at d = 128, so each K and V operand read
+// from LDS feeds two products; one at d = 64, so that a workgroup of one query
+// head covers 256 rows and short sequences still give many workgroups
+template <int D>
+constexpr int blocks_for() { return D == 128 ? 2 : 1; }
 constexpr int kRows = 32;   // query rows per wave
 constexpr int kBc = 64;     // keys per tile
 constexpr int kKPad = 8;    // K rows: stride = 4 banks mod 64, conflict-free 16-byte operand reads
@@ -88,6 +98,8 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     int nchunks, int nrb, int win, int o_bf16) {
     static_assert(!WINDOW || CAUSAL, "the sliding window is built for causal attention");
     constexpr int kWaves = waves_for<D>();
+    constexpr int NB = blocks_for<D>();
+    constexpr int WR = kRows * NB;      // query rows per wave
     constexpr int KS = D + kKPad;       // K row stride in LDS (elements)
     constexpr int VS = D + kVPad;       // V row stride in LDS (elements)
     constexpr int CPR = D / 8;          // 16-byte chunks per row
@@ -123,20 +135,24 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const bool active = (hc < hpw) && (hg < G);
     const int hq = g * G + (active ? hg : 0);
 
-    const int row0 = rb * wph * kRows;                 // first query row of the workgroup
-    const int wrow0 = row0 + sub * kRows;              // first query row of this wave
-    const int qi = wrow0 + l32;                        // this lane's query row
+    const int row0 = rb * wph * WR;                    // first query row of the workgroup
+    const int wrow0 = row0 + sub * WR;                 // first query row of this wave
     const int off = Nk - Nq;                           // position of query i is off + i
-    const int qpos = off + qi;
+    int qi[NB], qpos[NB], blk_first[NB], blk_lo[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        qi[nb] = wrow0 + 32 * nb + l32;                // this lane's query row in block nb
+        qpos[nb] = off + qi[nb];
+        blk_first[nb] = off + wrow0 + 32 * nb;
+        blk_lo[nb] = off + min(Nq - 1, wrow0 + 32 * nb + 31) - win + 1;
+    }
 
     int kend = Nk;
-    if (CAUSAL) kend = min(Nk, off + min(Nq, row0 + wph * kRows));
+    if (CAUSAL) kend = min(Nk, off + min(Nq, row0 + wph * WR));
     // window: the first key any row of the workgroup sees, rounded down to a tile
     const int kbeg = WINDOW ? max(0, off + row0 - win + 1) / kBc * kBc : 0;
     const int ntiles = (kend - kbeg + kBc - 1) / kBc;
-    const int wave_first = off + wrow0;                          // first row's position
-    const int wave_last = off + min(Nq - 1, wrow0 + kRows - 1);  // last key this wave may see
-    const int wave_lo = wave_last - win + 1;  // window: keys below this are hidden from some row
+    const int wave_last = off + min(Nq - 1, wrow0 + WR - 1);  // last key this wave may see
 
     const uint16_t* kbase = k + ((size_t)b * Hkv + g) * (size_t)Nk * D;
     const uint16_t* vbase = v + ((size_t)b * Hkv + g) * (size_t)Nk * D;
@@ -151,7 +167,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         const_cast<uint16_t*>(kbase), (short)0, Nk * D * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(vbase), (short)0, Nk * D * 2, 0x00020000);
-    auto dma = [&](__amdgpu_buffer_rsrc_t rsrc, uint16_t* dstbuf, int stride, int key0) {
+    auto dma = [&](__amdgpu_buffer_rsrc_t rsrc, uint16_t* dstbuf, int stride, int key0) __attribute__((always_inline)) {
         static_assert(kBc == 64, "one load instruction per 64 slots = per slot column");
         const int spr = stride / 8;  // 16-byte slots per padded row
         const int ninst = spr;       // kBc rows x spr slots / 64 lanes
@@ -172,11 +188,19 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     auto dma_wait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
 
     // ---- Q fragment (B operand of S^T = K Q^T): query l32, d = 16s + 8*half .. +7
+    // Q of block 0 in registers; of block 1 (if any) in this wave's LDS slice
+    // (row stride 4 banks mod 64: conflict-free 16-byte reads), written once
+    // here and read by this wave only (before any read the prologue barrier
+    // has passed)
+    constexpr int QS = D + kKPad;
+    __shared__ __attribute__((aligned(16))) uint16_t Qw[NB > 1 ? kWaves * 32 * QS : 8];
+    uint16_t* qw = Qw + (NB > 1 ? wave * 32 * QS : 0);
     bf16x8 qf[D / 16];
-    {
-        const bool ok = active && qi < Nq;
-        const uint16_t* qrow = q + (((size_t)b * Hq + hq) * Nq + (ok ? qi : 0)) * D;
-        const double2* trow = ROPE ? tab + (size_t)(ok ? qpos : 0) * (D / 2) : nullptr;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const bool ok = active && qi[nb] < Nq;
+        const uint16_t* qrow = q + (((size_t)b * Hq + hq) * Nq + (ok ? qi[nb] : 0)) * D;
+        const double2* trow = ROPE ? tab + (size_t)(ok ? qpos[nb] : 0) * (D / 2) : nullptr;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
             const int d0 = 16 * s + 8 * half;
@@ -185,20 +209,25 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                 x = *reinterpret_cast<const uint4*>(qrow + d0);
                 if (ROPE) x = rope8_bf16(x, trow, d0);
             }
-            qf[s] = __builtin_bit_cast(bf16x8, x);
+            if (nb == 0)
+                qf[s] = __builtin_bit_cast(bf16x8, x);
+            else
+                *reinterpret_cast<uint4*>(qw + l32 * QS + d0) = x;
         }
     }
 
-    f32x16 oacc[D / 32];
+    f32x16 oacc[NB][D / 32];
+    float m_run[NB], l_run[NB], r_run[NB], neg_m[NB], grow_at[NB];
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
-    float m_run = -INFINITY;   // reference max (log2 domain) of this lane's row
-    float l_run = 0.f;         // this lane's share of the row sum (fp32 weights): for lse
-    float r_run = 0.f;         // same sum of the bf16-rounded weights the MFMA used: for O
-    // refreshed only when the reference moves: -m (0 while m is -inf), and the
-    // raw row max above which the reference moves, (m + kLazy) / (scale log2 e)
-    float neg_m = 0.f;
-    float grow_at = -INFINITY;
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) oacc[nb][i] = f32x16{};
+        m_run[nb] = -INFINITY;   // reference max (log2 domain) of this lane's row
+        l_run[nb] = 0.f;         // this lane's share of the row sum (fp32 weights): for lse
+        r_run[nb] = 0.f;         // same sum of the bf16-rounded weights the MFMA used: for O
+        neg_m[nb] = 0.f;         // -m (0 while m is -inf)
+        grow_at[nb] = -INFINITY; // raw row max above which the reference moves
+    }
 
     // transposed-read addressing for the V operand (A of O^T += V^T P^T)
     const int grp = lane >> 4;          // 16-lane group
@@ -207,31 +236,13 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const int vcol_in = 16 * (grp & 1) + 4 * (w16 & 3);
     const int vkey_h = 4 * (grp >> 1);  // = 4 * half
 
-    // One online-softmax update over 32 keys held in LDS (rows Kt, Vt):
-    // S^T = K Q^T, mask, row max, rare rescale, weights, O^T += V^T P^T.
-    auto half_update = [&](const uint16_t* Kt, const uint16_t* Vt, int key0) {
-        f32x16 sc = f32x16{};
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kt[l32 * KS + 16 * s + 8 * half]);
-            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sc, 0, 0, 0);
-        }
-        const bool need_mask = (key0 + 32 > Nk) || (CAUSAL && key0 + 31 > wave_first) ||
-                               (WINDOW && key0 < wave_lo);
-        if (need_mask) {
-            keep_branch();
-            // element i holds key kl + c_i with c_i = 8 (i / 4) + i % 4: one
-            // per-lane bound on c_i instead of a key per element
-            const int kl = key0 + 4 * half;
-            const int hi = (CAUSAL ? min(qpos, Nk - 1) : Nk - 1) - kl;
-            const int lo = WINDOW ? qpos - win + 1 - kl : 0;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int ci = 8 * (i >> 2) + (i & 3);
-                const bool vis = ci <= hi && (!WINDOW || ci >= lo);
-                sc[i] = vis ? sc[i] : -INFINITY;
-            }
-        }
+    // One online-softmax update over 32 keys held in LDS (rows Kt, Vt) for
+    // the wave's NB row blocks: S^T = K Q^T (each K operand feeds every block),
+    // mask, row max, rare rescale, weights, O^T += V^T P^T (each V operand feeds
+    // every block).  The helpers are forced inline: left as calls, the blocks'
+    // accumulators would live in memory.
+    auto softmax = [&](f32x16& sc, f32x16 (&oa)[D / 32], float& m_r, float& l_r, float& r_r,
+                       float& nm, float& ga, uint4 (&pw)[2]) __attribute__((always_inline)) {
         // row max as one chain of three-input maxima (v_max3_f32)
         float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
 #pragma unroll
@@ -248,46 +259,79 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             asm volatile("" : "+v"(lo), "+v"(hi));
             mx = fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
         }
-        const bool grow = mx > grow_at;
+        const bool grow = mx > ga;
         if (__ballot(grow)) {
             keep_branch();
-            const float m_new = grow ? mx * scale_log2 : m_run;
-            const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
-            l_run *= alpha;
-            r_run *= alpha;
+            const float m_new = grow ? mx * scale_log2 : m_r;
+            const float alpha = grow ? fast_exp2(m_r - m_new) : 1.f;
+            l_r *= alpha;
+            r_r *= alpha;
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-            m_run = m_new;
-            neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
-            grow_at = (m_run + kLazy) / scale_log2;
+            for (int db = 0; db < D / 32; ++db) oa[db] *= alpha;
+            m_r = m_new;
+            nm = (m_new == -INFINITY) ? 0.f : -m_new;
+            ga = (m_new + kLazy) / scale_log2;
         }
-        // the weights are the one stretch of pure vector work: raising the
-        // wave's issue priority here lets it finish them while the other waves
-        // of the SIMD keep the matrix cores fed (measured +1.5%; raising it
-        // around the products instead loses 3.5%)
+        // the weights are the one stretch of pure vector work: the wave raises
+        // its issue priority for it, so the other wave of the SIMD gets the
+        // matrix cores around it
         __builtin_amdgcn_s_setprio(1);
-        uint4 pw[2];
 #pragma unroll
         for (int ss = 0; ss < 2; ++ss) {
             float p[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                p[e] = fast_exp2(fmaf(sc[8 * ss + e], scale_log2, neg_m));
-                l_run += p[e];
+                p[e] = fast_exp2(fmaf(sc[8 * ss + e], scale_log2, nm));
+                l_r += p[e];
             }
             pw[ss].x = pack_bf16x2(p[0], p[1]);
             pw[ss].y = pack_bf16x2(p[2], p[3]);
             pw[ss].z = pack_bf16x2(p[4], p[5]);
             pw[ss].w = pack_bf16x2(p[6], p[7]);
-            r_run = sum_bf16x2(pw[ss].x, r_run);
-            r_run = sum_bf16x2(pw[ss].y, r_run);
-            r_run = sum_bf16x2(pw[ss].z, r_run);
-            r_run = sum_bf16x2(pw[ss].w, r_run);
+            r_r = sum_bf16x2(pw[ss].x, r_r);
+            r_r = sum_bf16x2(pw[ss].y, r_r);
+            r_r = sum_bf16x2(pw[ss].z, r_r);
+            r_r = sum_bf16x2(pw[ss].w, r_r);
         }
         __builtin_amdgcn_s_setprio(0);
+    };
+    auto half_update = [&](const uint16_t* Kt, const uint16_t* Vt, int key0) __attribute__((always_inline)) {
+        f32x16 sc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) sc[nb] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kt[l32 * KS + 16 * s + 8 * half]);
+            sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sc[0], 0, 0, 0);
+            if constexpr (NB > 1) {
+                const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(&qw[l32 * QS + 16 * s + 8 * half]);
+                sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, sc[1], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const bool need_mask = (key0 + 32 > Nk) || (CAUSAL && key0 + 31 > blk_first[nb]) ||
+                                   (WINDOW && key0 < blk_lo[nb]);
+            if (need_mask) {
+                keep_branch();
+                // element i holds key kl + c_i with c_i = 8 (i / 4) + i % 4
+                const int kl = key0 + 4 * half;
+                const int hi = (CAUSAL ? min(qpos[nb], Nk - 1) : Nk - 1) - kl;
+                const int lo = WINDOW ? qpos[nb] - win + 1 - kl : 0;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int ci = 8 * (i >> 2) + (i & 3);
+                    const bool vis = ci <= hi && (!WINDOW || ci >= lo);
+                    sc[nb][i] = vis ? sc[nb][i] : -INFINITY;
+                }
+            }
+        }
+        uint4 pw[NB][2];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            softmax(sc[nb], oacc[nb], m_run[nb], l_run[nb], r_run[nb], neg_m[nb], grow_at[nb], pw[nb]);
 #pragma unroll
         for (int ss = 0; ss < 2; ++ss) {
-            const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[ss]);
             const int kbase_l = 16 * ss + vkey_h + vrow_in;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
@@ -296,13 +340,16 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                 const s16x4 hi = lds_read_tr(vp + 8 * VS);
                 const bf16x8 a = __builtin_bit_cast(
                     bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    oacc[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        a, __builtin_bit_cast(bf16x8, pw[nb][ss]), oacc[nb][db], 0, 0, 0);
             }
         }
     };
     // Tile t (64 keys in buffer P = t & 1, a constant at every call): two
     // updates, while K/V(t+1) arrive in the other buffer.
-    auto step = [&](int t, int P) {
+    auto step = [&](int t, int P) __attribute__((always_inline)) {
         const int key0 = kbeg + t * kBc;
         // K/V(t+1) replace K/V(t-1), last read before the previous barrier
         dma(rk, kbuf(P ^ 1), KS, key0 + kBc);
@@ -326,29 +373,34 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
     if (t < ntiles) step(t, 0);
 
-    if (!active || qi >= Nq) return;
-    // O is the convex combination with the weights the MFMA actually used (their
-    // bf16 roundings), so it is normalised by their sum; lse uses the fp32 sum.
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float r_tot = r_run + __shfl_xor(r_run, 32);
-    const float inv = 1.f / r_tot;
-    const size_t orow = (((size_t)b * Hq + hq) * Nq + qi) * D;
+    if (!active) return;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int nb = 0; nb < NB; ++nb) {
+        if (qi[nb] >= Nq) continue;
+        // O is the convex combination with the weights the MFMA actually used
+        // (their bf16 roundings), so it is normalised by their sum; lse uses the
+        // fp32 sum.
+        const float l_tot = l_run[nb] + __shfl_xor(l_run[nb], 32);
+        const float r_tot = r_run[nb] + __shfl_xor(r_run[nb], 32);
+        const float inv = 1.f / r_tot;
+        const size_t orow = (((size_t)b * Hq + hq) * Nq + qi[nb]) * D;
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-            const int d = 32 * db + 8 * i4 + 4 * half;
-            float4 r = make_float4(oacc[db][4 * i4 + 0] * inv, oacc[db][4 * i4 + 1] * inv,
-                                   oacc[db][4 * i4 + 2] * inv, oacc[db][4 * i4 + 3] * inv);
-            if (o_bf16)  // the fp32 value rounded to the nearest bf16 (even on ties)
-                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(o) + orow + d) =
-                    make_uint2(pack_bf16x2(r.x, r.y), pack_bf16x2(r.z, r.w));
-            else
-                *reinterpret_cast<float4*>(static_cast<float*>(o) + orow + d) = r;
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int d = 32 * db + 8 * i4 + 4 * half;
+                float4 r = make_float4(oacc[nb][db][4 * i4 + 0] * inv, oacc[nb][db][4 * i4 + 1] * inv,
+                                       oacc[nb][db][4 * i4 + 2] * inv, oacc[nb][db][4 * i4 + 3] * inv);
+                if (o_bf16)
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(o) + orow + d) =
+                        make_uint2(pack_bf16x2(r.x, r.y), pack_bf16x2(r.z, r.w));
+                else
+                    *reinterpret_cast<float4*>(static_cast<float*>(o) + orow + d) = r;
+            }
         }
+        if (lse != nullptr && half == 0)
+            lse[((size_t)b * Hq + hq) * Nq + qi[nb]] = (m_run[nb] + fast_log2(l_tot)) * kLn2;
     }
-    if (lse != nullptr && half == 0)
-        lse[((size_t)b * Hq + hq) * Nq + qi] = (m_run + fast_log2(l_tot)) * kLn2;
 }
 
 template <int D, bool CAUSAL, bool ROPE, bool WINDOW>
@@ -362,7 +414,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
         if (kWaves % c == 0 && G % c == 0) hpw = c;
     const int wph = kWaves / hpw;                      // waves per head
     const int nchunks = (G + hpw - 1) / hpw;
-    const int rows_per_wg = wph * kRows;
+    const int rows_per_wg = wph * kRows * blocks_for<D>();
     const int nrb = (a.Nq + rows_per_wg - 1) / rows_per_wg;
     const long long nwg = (long long)nrb * a.B * a.Hkv * nchunks;
     if (nwg == 0) return hipSuccess;
