@@ -236,67 +236,69 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const int vcol_in = 16 * (grp & 1) + 4 * (w16 & 3);
     const int vkey_h = 4 * (grp >> 1);  // = 4 * half
 
-    // One online-softmax update over 32 keys held in LDS (rows Kt, Vt) for
-    // the wave's NB row blocks: S^T = K Q^T (each K operand feeds every block),
-    // mask, row max, rare rescale, weights, O^T += V^T P^T (each V operand feeds
-    // every block).  The helpers are forced inline: left as calls, the blocks'
-    // accumulators would live in memory.
-    auto softmax = [&](f32x16& sc, f32x16 (&oa)[D / 32], float& m_r, float& l_r, float& r_r,
-                       float& nm, float& ga, uint4 (&pw)[2]) __attribute__((always_inline)) {
-        // row max as one chain of three-input maxima (v_max3_f32)
-        float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
-#pragma unroll
-        for (int i = 3; i + 1 < 16; i += 2) mx = fmaxf(fmaxf(mx, sc[i]), sc[i + 1]);
-        mx = fmaxf(mx, sc[15]);
-        {
-            // the other half's max: v_permlane32_swap gives lanes 0-31 (r[0])
-            // and lanes 32-63 (r[1]) in both halves, with no LDS round trip
-            const unsigned u = __builtin_bit_cast(unsigned, mx);
-            const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-            // opaque to the optimiser: left visible, the max of the two results
-            // is folded into the first one alone
-            unsigned lo = r[0], hi = r[1];
-            asm volatile("" : "+v"(lo), "+v"(hi));
-            mx = fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
-        }
-        const bool grow = mx > ga;
-        if (__ballot(grow)) {
+    // ---- the pieces of an online-softmax update over 32 keys (forced inline:
+    //      left as calls, the blocks' accumulators would live in memory)
+    // the element mask of block x for the 32 keys from key0 (a uniform branch:
+    // only blocks that cross the diagonal, the window edge or the end of K)
+    auto mask = [&](int x, f32x16& s, int key0) __attribute__((always_inline)) {
+        const bool need_mask = (key0 + 32 > Nk) || (CAUSAL && key0 + 31 > blk_first[x]) ||
+                               (WINDOW && key0 < blk_lo[x]);
+        if (need_mask) {
             keep_branch();
-            const float m_new = grow ? mx * scale_log2 : m_r;
-            const float alpha = grow ? fast_exp2(m_r - m_new) : 1.f;
-            l_r *= alpha;
-            r_r *= alpha;
+            // element i holds key kl + c_i with c_i = 8 (i / 4) + i % 4
+            const int kl = key0 + 4 * half;
+            const int hi = (CAUSAL ? min(qpos[x], Nk - 1) : Nk - 1) - kl;
+            const int lo = WINDOW ? qpos[x] - win + 1 - kl : 0;
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) oa[db] *= alpha;
-            m_r = m_new;
-            nm = (m_new == -INFINITY) ? 0.f : -m_new;
-            ga = (m_new + kLazy) / scale_log2;
+            for (int i = 0; i < 16; ++i) {
+                const int ci = 8 * (i >> 2) + (i & 3);
+                const bool vis = ci <= hi && (!WINDOW || ci >= lo);
+                s[i] = vis ? s[i] : -INFINITY;
+            }
         }
-        // the weights are the one stretch of pure vector work: the wave raises
-        // its issue priority for it, so the other wave of the SIMD gets the
-        // matrix cores around it
-        __builtin_amdgcn_s_setprio(1);
+    };
+    // row max of the 16 scores a lane holds and of the other half's 16: a tree
+    // of three-input maxima (depth 3), then one exchange between the halves
+    auto rowmax = [&](const f32x16& s) __attribute__((always_inline)) {
+        const float a = fmaxf(fmaxf(s[0], s[1]), s[2]);
+        const float b = fmaxf(fmaxf(s[3], s[4]), s[5]);
+        const float c = fmaxf(fmaxf(s[6], s[7]), s[8]);
+        const float d = fmaxf(fmaxf(s[9], s[10]), s[11]);
+        const float e = fmaxf(fmaxf(s[12], s[13]), s[14]);
+        float mx = fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), s[15]));
+        // the other half's max: v_permlane32_swap gives lanes 0-31 (r[0])
+        // and lanes 32-63 (r[1]) in both halves, with no LDS round trip
+        const unsigned u = __builtin_bit_cast(unsigned, mx);
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        // opaque to the optimiser: left visible, the max of the two results
+        // is folded into the first one alone
+        unsigned lo = r[0], hi = r[1];
+        asm volatile("" : "+v"(lo), "+v"(hi));
+        return fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
+    };
+    // weights p = 2^(s scale log2(e) - m), their fp32 sum (pairwise), their
+    // bf16 packing and the sum of the packed values (two chains)
+    auto expo = [&](int x, const f32x16& sc, uint4 (&pw)[2]) __attribute__((always_inline)) {
+        float lsum[2], rsum[2];
 #pragma unroll
         for (int ss = 0; ss < 2; ++ss) {
             float p[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                p[e] = fast_exp2(fmaf(sc[8 * ss + e], scale_log2, nm));
-                l_r += p[e];
-            }
+            for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(sc[8 * ss + e], scale_log2, neg_m[x]));
+            lsum[ss] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
             pw[ss].x = pack_bf16x2(p[0], p[1]);
             pw[ss].y = pack_bf16x2(p[2], p[3]);
             pw[ss].z = pack_bf16x2(p[4], p[5]);
             pw[ss].w = pack_bf16x2(p[6], p[7]);
-            r_r = sum_bf16x2(pw[ss].x, r_r);
-            r_r = sum_bf16x2(pw[ss].y, r_r);
-            r_r = sum_bf16x2(pw[ss].z, r_r);
-            r_r = sum_bf16x2(pw[ss].w, r_r);
+            rsum[ss] = sum_bf16x2(pw[ss].w, sum_bf16x2(pw[ss].z, sum_bf16x2(pw[ss].y, sum_bf16x2(pw[ss].x, 0.f))));
         }
-        __builtin_amdgcn_s_setprio(0);
+        l_run[x] += lsum[0] + lsum[1];
+        r_run[x] += rsum[0] + rsum[1];
     };
-    auto half_update = [&](const uint16_t* Kt, const uint16_t* Vt, int key0) __attribute__((always_inline)) {
-        f32x16 sc[NB];
+    f32x16 sc[NB];
+    uint4 pw[NB][2];
+    // S_x^T = K Q_x^T for every block x; each K operand feeds all of them
+    auto qk_all = [&](const uint16_t* Kt) __attribute__((always_inline)) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) sc[nb] = f32x16{};
 #pragma unroll
@@ -308,28 +310,9 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                 sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, sc[1], 0, 0, 0);
             }
         }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const bool need_mask = (key0 + 32 > Nk) || (CAUSAL && key0 + 31 > blk_first[nb]) ||
-                                   (WINDOW && key0 < blk_lo[nb]);
-            if (need_mask) {
-                keep_branch();
-                // element i holds key kl + c_i with c_i = 8 (i / 4) + i % 4
-                const int kl = key0 + 4 * half;
-                const int hi = (CAUSAL ? min(qpos[nb], Nk - 1) : Nk - 1) - kl;
-                const int lo = WINDOW ? qpos[nb] - win + 1 - kl : 0;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int ci = 8 * (i >> 2) + (i & 3);
-                    const bool vis = ci <= hi && (!WINDOW || ci >= lo);
-                    sc[nb][i] = vis ? sc[nb][i] : -INFINITY;
-                }
-            }
-        }
-        uint4 pw[NB][2];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            softmax(sc[nb], oacc[nb], m_run[nb], l_run[nb], r_run[nb], neg_m[nb], grow_at[nb], pw[nb]);
+    };
+    // O_x^T += V^T P_x^T for every block x; each V operand feeds all of them
+    auto pv_all = [&](const uint16_t* Vt) __attribute__((always_inline)) {
 #pragma unroll
         for (int ss = 0; ss < 2; ++ss) {
             const int kbase_l = 16 * ss + vkey_h + vrow_in;
@@ -347,18 +330,64 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             }
         }
     };
-    // Tile t (64 keys in buffer P = t & 1, a constant at every call): two
-    // updates, while K/V(t+1) arrive in the other buffer.
+    // the weights of every block for the 32 keys from key0: masks, then the
+    // row maxima of all blocks, one rescale decision for all of them (a block
+    // whose reference does not move takes alpha = 1), then all weights, so
+    // the independent chains of the blocks interleave
+    auto sm_all = [&](int key0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) mask(nb, sc[nb], key0);
+        float mx[NB];
+        bool grow[NB];
+        bool any = false;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            mx[nb] = rowmax(sc[nb]);
+            grow[nb] = mx[nb] > grow_at[nb];
+            any = any || grow[nb];
+        }
+        if (__ballot(any)) {
+            keep_branch();
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const float m_new = grow[nb] ? mx[nb] * scale_log2 : m_run[nb];
+                const float alpha = grow[nb] ? fast_exp2(m_run[nb] - m_new) : 1.f;
+                l_run[nb] *= alpha;
+                r_run[nb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) oacc[nb][db] *= alpha;
+                m_run[nb] = m_new;
+                neg_m[nb] = (m_new == -INFINITY) ? 0.f : -m_new;
+                grow_at[nb] = (m_new + kLazy) / scale_log2;
+            }
+        }
+        // the weights are the one long stretch of pure vector work: the wave
+        // raises its issue priority for it, so the other wave of the SIMD gets
+        // the matrix cores around it
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) expo(nb, sc[nb], pw[nb]);
+        __builtin_amdgcn_s_setprio(0);
+    };
+    // One online-softmax update over 32 keys held in LDS (rows Kt, Vt) for
+    // the wave's row blocks; tile t (64 keys in buffer P = t & 1, a constant
+    // at every call) takes two of them while K/V(t+1) arrive in the other
+    // buffer.
     auto step = [&](int t, int P) __attribute__((always_inline)) {
         const int key0 = kbeg + t * kBc;
         // K/V(t+1) replace K/V(t-1), last read before the previous barrier
         dma(rk, kbuf(P ^ 1), KS, key0 + kBc);
         dma(rv, vbuf(P ^ 1), VS, key0 + kBc);
-        half_update(kbuf(P), vbuf(P), key0);
+        qk_all(kbuf(P));
+        sm_all(key0);
+        pv_all(vbuf(P));
         // the second half is skipped when no key of it is visible to any row of
         // the wave (causal tail, end of K)
-        if (key0 + 32 < Nk && (!CAUSAL || key0 + 32 <= wave_last))
-            half_update(kbuf(P) + 32 * KS, vbuf(P) + 32 * VS, key0 + 32);
+        if (key0 + 32 < Nk && (!CAUSAL || key0 + 32 <= wave_last)) {
+            qk_all(kbuf(P) + 32 * KS);
+            sm_all(key0 + 32);
+            pv_all(vbuf(P) + 32 * VS);
+        }
         dma_wait();
         __syncthreads();
     };
