@@ -258,7 +258,17 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     };
     // P and dS of one tile, then dV += P^T dO and dK += dS^T Q over its 32
     // queries (two k-steps)
-    auto accumulate = [&](int buf, int sub, int q0, const f32x16& sa, const f32x16& pa) {
+    auto accumulate = [&](int buf, int sub, int q0, f32x16& sa, const f32x16& pa) {
+        // the element mask, only where the update's queries cross this wave's
+        // diagonal or its keys run past the end of K (a uniform branch): a
+        // hidden pair's score becomes -inf, so its P = 2^-inf = 0
+        if (kw0 + kKeysW > Nk || (CAUSAL && q0 + off < kw0 + kKeysW - 1)) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int qi = q0 + perm16(8 * (i >> 2) + 4 * half + (i & 3));
+                sa[i] = qi >= qmin ? sa[i] : -INFINITY;
+            }
+        }
         uint32_t pw[2][4], dw[2][4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -268,10 +278,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 4 * j + e;
-                const int qi = q0 + perm16(8 * j + 4 * half + e);
-                // branch-free: a hidden pair gets 2^-inf = 0
-                const float x = fmaf(sa[i], scale_log2, -l4[e]);
-                p[e] = fast_exp2(qi >= qmin ? x : -INFINITY);
+                p[e] = fast_exp2(fmaf(sa[i], scale_log2, -l4[e]));
                 ds[e] = p[e] * (pa[i] - d4[e]);
             }
             pw[j >> 1][2 * (j & 1)] = pack_bf16x2(p[0], p[1]);
@@ -411,6 +418,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int klast = CAUSAL ? min(Nk - 1, qpos) : Nk - 1;  // last key this row sees
     // last key any row of this wave sees (causal): later 32-key halves are skipped
     const int wave_klast = off + min(Nq - 1, row0 + sub * kRows + kRows - 1);
+    // last key every row of this wave sees (causal): keys up to it need no mask
+    const int wave_kfirst = off + row0 + sub * kRows;
     int kend = Nk;
     if (CAUSAL) kend = min(Nk, off + min(Nq, row0 + wph * kRows));
     const int ntiles = (kend + kBc - 1) / kBc;
@@ -488,6 +497,15 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Vt[(kb * 32 + prow) * VS + 16 * s + 8 * half]);
                 pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[s], pacc, 0, 0, 0);
             }
+            // the element mask, only where these keys cross the diagonal of the
+            // wave's first row or run past the end of K (a uniform branch)
+            if (key0 + 32 * kb + 31 >= Nk || (CAUSAL && key0 + 32 * kb + 31 > wave_kfirst)) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int kk = key0 + kb * 32 + perm16(8 * (i >> 2) + 4 * half + (i & 3));
+                    sacc[i] = kk <= klast ? sacc[i] : -INFINITY;
+                }
+            }
             uint32_t da[2][4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -495,10 +513,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = 4 * j + e;
-                    const int kk = key0 + kb * 32 + perm16(8 * j + 4 * half + e);
-                    // branch-free: a hidden pair gets 2^-inf = 0
-                    const float x = fmaf(sacc[i], scale_log2, -lrow);
-                    const float p = fast_exp2(kk <= klast ? x : -INFINITY);
+                    const float p = fast_exp2(fmaf(sacc[i], scale_log2, -lrow));
                     ds[e] = p * (pacc[i] - drow);
                 }
                 da[j >> 1][2 * (j & 1)] = pack_bf16x2(ds[0], ds[1]);
