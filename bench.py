@@ -93,6 +93,129 @@ def recorded_clock(kernel: str):
 
 METRIC = "attn fwd TFLOP/s (causal GQA N=8192 d=128 bf16) + decode HBM GB/s"
 
+# ---- writing the counter records from rocprofv3 output (CSV)
+XCDS = 8  # MI355X: GRBM_GUI_ACTIVE arrives summed over its eight dies
+
+
+def short_kernel_name(full: str) -> str:
+    """'void attn::(anonymous namespace)::k<128, true>(int, ...)' -> 'k<128, true>'."""
+    s = full
+    for p in ("void ", "attn::", "(anonymous namespace)::"):
+        s = s.replace(p, "")
+    depth = 0
+    for i, ch in enumerate(s):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return s[:i]
+    return s
+
+
+def read_counters(path: str):
+    """Per dispatch: kernel name, grid size, duration (ns) and each counter
+    summed over the rows rocprofv3 wrote for it (one per die or instance)."""
+    import csv
+    import collections
+    out = collections.OrderedDict()
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = int(r["Dispatch_Id"])
+            e = out.setdefault(d, {"name": short_kernel_name(r["Kernel_Name"]),
+                                   "grid": int(r["Grid_Size"]),
+                                   "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
+                                   "c": collections.defaultdict(float)})
+            e["c"][r["Counter_Name"]] += float(r["Counter_Value"])
+    return list(out.values())
+
+
+def _counter_csv(d: str) -> str:
+    import glob
+    hits = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+    if not hits:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return hits[0]
+
+
+def _mean_by(dispatches, counter, key):
+    import collections
+    acc = collections.defaultdict(list)
+    for e in dispatches:
+        if counter in e["c"]:
+            acc[key(e)].append(e["c"][counter])
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def write_traffic_record(d: str):
+    """profiles/traffic.json from rocprofv3 --pmc runs under ``d``: fetch/ and
+    write/ (FETCH_SIZE, WRITE_SIZE over 'bench.py --steps 1 --warmup 0
+    --no-cpu-baseline --no-extra'), xfetch/ and xwrite/ (the same without
+    --no-extra, optional), cal_fetch/ and cal_write/ ('bench.py
+    --calibrate-copy')."""
+    def load(sub):
+        p = os.path.join(d, sub)
+        return read_counters(_counter_csv(p)) if os.path.isdir(p) else None
+    f, w_ = load("fetch"), load("write")
+    cf, cw = load("cal_fetch"), load("cal_write")
+    name = lambda e: e["name"]
+    copy = "__amd_rocclr_copyBuffer"
+    cfk = _mean_by(cf, "FETCH_SIZE", name)[copy]
+    cwk = _mean_by(cw, "WRITE_SIZE", name)[copy]
+    nbytes = 1 << 30
+    fk, wk = _mean_by(f, "FETCH_SIZE", name), _mean_by(w_, "WRITE_SIZE", name)
+    rec = {
+        "source_hash": source_hash(),
+        "note": "per-dispatch FETCH_SIZE and WRITE_SIZE (KiB, mean over dispatches) from two "
+                "rocprofv3 --pmc passes over 'python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline "
+                "--no-extra' (kernels of the headline step); 'extras' from the same passes without "
+                "--no-extra, keyed by kernel and grid size; calibration: a 1 GiB device copy "
+                "('python3 bench.py --calibrate-copy') reads as the counts below",
+        "calibration": {"copy_bytes": nbytes, "copy_fetch_kib": cfk, "copy_write_kib": cwk,
+                        "fetch_factor": nbytes / (cfk * 1024.0), "write_factor": nbytes / (cwk * 1024.0)},
+        "kernels": {k: {"fetch_kib": fk[k], "write_kib": wk[k]} for k in sorted(fk)
+                    if k in wk and not k.startswith("__amd")},
+    }
+    xf, xw = load("xfetch"), load("xwrite")
+    if xf and xw:
+        key = lambda e: f"{e['name']} @grid {e['grid']}"
+        a, b = _mean_by(xf, "FETCH_SIZE", key), _mean_by(xw, "WRITE_SIZE", key)
+        rec["extras"] = {k: {"fetch_kib": a[k], "write_kib": b[k]} for k in sorted(a)
+                         if k in b and not k.startswith("__amd")}
+    with open(TRAFFIC_RECORD, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(f"wrote {TRAFFIC_RECORD}")
+
+
+def write_clock_record(d: str):
+    """profiles/clock.json from a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
+    GRBM_GUI_ACTIVE run under ``d`` over the headline step: the shader clock is
+    GPU-active cycles per die over the dispatch time; the matrix-core busy
+    fraction is MFMA-busy cycles over active cycles x 1024 SIMDs."""
+    ds = read_counters(_counter_csv(d))
+    import collections
+    per = collections.defaultdict(list)
+    for e in ds:
+        c = e["c"]
+        # a short dispatch's active count takes in cycles outside it: only
+        # kernels of 100 us and more are kept
+        if "GRBM_GUI_ACTIVE" in c and "SQ_VALU_MFMA_BUSY_CYCLES" in c and e["ns"] >= 100000:
+            act = c["GRBM_GUI_ACTIVE"] / XCDS
+            per[e["name"]].append((act / e["ns"], 100.0 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (act * 1024)))
+    rec = {
+        "source_hash": source_hash(),
+        "note": "shader clock under each kernel: GRBM_GUI_ACTIVE (summed over the 8 dies, so divided by 8) "
+                "per dispatch over its duration, mean over dispatches (kernels of 100 us and more); mfma_util_pct = "
+                "SQ_VALU_MFMA_BUSY_CYCLES / (active cycles x 1024 SIMDs); from rocprofv3 --pmc "
+                "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE over 'python3 bench.py --steps 2 --warmup 1 "
+                "--no-cpu-baseline --no-extra'",
+        "kernels": {k: {"sclk_ghz": sum(x[0] for x in v) / len(v),
+                        "mfma_util_pct": sum(x[1] for x in v) / len(v)} for k, v in sorted(per.items())},
+    }
+    with open(CLOCK_RECORD, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(f"wrote {CLOCK_RECORD}")
+
 
 def visible_pairs(Nq, Nk, causal, window=0):
     if not causal:
@@ -195,9 +318,10 @@ def cpu_baseline(w3, w4, budget_s=20.0):
         "value": tflops, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
         "sample": f"prefill: {heads} of {total} whole query heads (8192 rows each) of the causal "
                   f"GQA RoPE N=8192 workload in {t_pf:.1f} s on {cores} worker processes of one "
-                  f"BLAS thread each (fp64 NumPy, RoPE rounding model, dense score rows); rate "
-                  f"extrapolated to the workload from those heads; decode: {len(lens)} whole "
-                  f"sequences of the decode workload in {t_dec:.1f} s",
+                  f"BLAS thread each (fp64 NumPy, RoPE rounding model, dense score rows)"
+                  + ("" if heads == total else "; the rate over those heads stands for the workload")
+                  + f"; decode: {len(lens)} of the {w4.B} sequences of the decode workload in "
+                  f"{t_dec:.1f} s, the rate over them standing for the workload",
         "extrapolated": heads < total,
         "decode_value": nbytes / t_dec / 1e9, "decode_unit": "GB/s",
     }
@@ -348,7 +472,17 @@ def main():
                     help="skip the extra prefill workloads (MHA d=64 N=2048, GQA N=32768, sliding window)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy three times (counter calibration)")
+    ap.add_argument("--write-traffic-record", metavar="DIR",
+                    help="write profiles/traffic.json from rocprofv3 --pmc output under DIR (no GPU)")
+    ap.add_argument("--write-clock-record", metavar="DIR",
+                    help="write profiles/clock.json from rocprofv3 --pmc output under DIR (no GPU)")
     args = ap.parse_args()
+    if args.write_traffic_record or args.write_clock_record:
+        if args.write_traffic_record:
+            write_traffic_record(args.write_traffic_record)
+        if args.write_clock_record:
+            write_clock_record(args.write_clock_record)
+        return
     if args.calibrate_copy:
         import torch
         n = (1 << 30) // 4
