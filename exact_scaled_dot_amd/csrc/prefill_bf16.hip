@@ -257,17 +257,18 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             }
         }
     };
-    // row max of the 16 scores a lane holds and of the other half's 16: a tree
-    // of three-input maxima (depth 3), then one exchange between the halves
-    auto rowmax = [&](const f32x16& s) __attribute__((always_inline)) {
+    // max of the 16 scores a lane holds: a tree of three-input maxima (depth 3)
+    auto lanemax = [&](const f32x16& s) __attribute__((always_inline)) {
         const float a = fmaxf(fmaxf(s[0], s[1]), s[2]);
         const float b = fmaxf(fmaxf(s[3], s[4]), s[5]);
         const float c = fmaxf(fmaxf(s[6], s[7]), s[8]);
         const float d = fmaxf(fmaxf(s[9], s[10]), s[11]);
         const float e = fmaxf(fmaxf(s[12], s[13]), s[14]);
-        float mx = fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), s[15]));
-        // the other half's max: v_permlane32_swap gives lanes 0-31 (r[0])
-        // and lanes 32-63 (r[1]) in both halves, with no LDS round trip
+        return fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), s[15]));
+    };
+    // the row max from the two halves' maxima: v_permlane32_swap gives lanes
+    // 0-31 (r[0]) and lanes 32-63 (r[1]) in both halves, with no LDS round trip
+    auto rowmax = [&](float mx) __attribute__((always_inline)) {
         const unsigned u = __builtin_bit_cast(unsigned, mx);
         const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
         // opaque to the optimiser: left visible, the max of the two results
@@ -337,21 +338,24 @@ prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     auto sm_all = [&](int key0) __attribute__((always_inline)) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) mask(nb, sc[nb], key0);
+        // a lane's own half of a row decides whether the wave takes the rescale
+        // path; only there is the row max formed across the halves, so that
+        // both halves of a row move their reference together
         float mx[NB];
-        bool grow[NB];
         bool any = false;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            mx[nb] = rowmax(sc[nb]);
-            grow[nb] = mx[nb] > grow_at[nb];
-            any = any || grow[nb];
+            mx[nb] = lanemax(sc[nb]);
+            any = any || mx[nb] > grow_at[nb];
         }
         if (__ballot(any)) {
             keep_branch();
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const float m_new = grow[nb] ? mx[nb] * scale_log2 : m_run[nb];
-                const float alpha = grow[nb] ? fast_exp2(m_run[nb] - m_new) : 1.f;
+                mx[nb] = rowmax(mx[nb]);
+                const bool grow = mx[nb] > grow_at[nb];
+                const float m_new = grow ? mx[nb] * scale_log2 : m_run[nb];
+                const float alpha = grow ? fast_exp2(m_run[nb] - m_new) : 1.f;
                 l_run[nb] *= alpha;
                 r_run[nb] *= alpha;
 #pragma unroll
