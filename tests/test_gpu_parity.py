@@ -208,9 +208,10 @@ def _block_edge_rows(N, rows_per_block, rng, n_blocks, n_random):
 
 def test_gqa_rope_n32768_all_heads_block_edges():
     """Long-context GQA + RoPE 5e5, B=1 Hq=64 Hkv=8 N=32768 d=128, Q,K ~ N(0,16):
-    all 64 heads, each on at least 128 rows at both edges of 96-row workgroup
-    blocks (4 heads x 3 waves of 32 rows share a KV head's tiles) and of the
-    wave blocks inside them, at blocks sampled per head."""
+    all 64 heads, each on at least 128 rows at both edges of 64-row workgroup
+    blocks (the 8 query heads of a KV head share its tiles in one workgroup,
+    one wave of 64 rows per head) and of the two 32-row blocks of each wave,
+    at blocks sampled per head."""
     w = W.WORKLOADS["gqa_rope_n32768"]
     q, k, v = W.fwd_inputs(w)
     say(f"{w.name}: {w.note}")
@@ -219,7 +220,7 @@ def test_gqa_rope_n32768_all_heads_block_edges():
     kc = {}
     eo = el = 0.0
     for h in range(w.Hq):
-        rows = _block_edge_rows(w.Nq, 96, rng, 20, 12)
+        rows = _block_edge_rows(w.Nq, 64, rng, 32, 12)
         assert len(rows) >= 128, len(rows)
         ro, rl = oa.attention_rows(q, k, v, 0, h, rows, causal=True, scale=w.scale,
                                    rope_base=w.rope_base, dtype=w.dtype, _kcache=kc)
