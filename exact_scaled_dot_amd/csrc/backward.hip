@@ -187,7 +187,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     // the first query row that sees this key (past the end of K: none)
     const int qmin = key < Nk ? (CAUSAL ? key - off : 0) : 0x7fffffff;
     struct Pair {
-        float l, d;  // this thread's slot of the tile's statistics
+        float l, d;  // this thread's slot of the tile's statistics: lse (log2) and -D
     };
     // One copy of a 32-row tile into LDS: instruction j writes 16-byte slots
     // 64 j .. 64 j + 63, slot s holding row s / SPR, chunk s % SPR of the
@@ -232,7 +232,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const int qr = q0 + perm16(lane);
         r.l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, qr * 4, 0, 0)) +
               (qr < Nq ? 0.f : INFINITY);
-        r.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, qr * 4, 0, 0));
+        r.d = -__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, qr * 4, 0, 0));
     };
     auto store_stats = [&](int buf, const Pair& r) {
         Ls[buf][lane] = r.l;
@@ -244,7 +244,13 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int prow = perm16(l32);  // tile row of this lane's A operand
     auto scores = [&](int buf, int sub, f32x16& sa, f32x16& pa) {
         sa = f32x16{};
-        pa = f32x16{};
+        // dP accumulates onto -D, so the products leave dP - D
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Dsh[buf][kQS * sub + 8 * j + 4 * half]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pa[4 * j + e] = d4[e];
+        }
         const uint16_t* Qb = Qr(buf) + kQS * RS * sub;
         const uint16_t* Ob = Or(buf) + kQS * RS * sub;
 #pragma unroll
@@ -273,13 +279,12 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][kQS * sub + 8 * j + 4 * half]);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Dsh[buf][kQS * sub + 8 * j + 4 * half]);
             float p[4], ds[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 4 * j + e;
                 p[e] = fast_exp2(fmaf(sa[i], scale_log2, -l4[e]));
-                ds[e] = p[e] * (pa[i] - d4[e]);
+                ds[e] = p[e] * pa[i];
             }
             pw[j >> 1][2 * (j & 1)] = pack_bf16x2(p[0], p[1]);
             pw[j >> 1][2 * (j & 1) + 1] = pack_bf16x2(p[2], p[3]);
@@ -439,6 +444,10 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
     const float lrow = ok ? lse2[qrow] : INFINITY;
     const float drow = ok ? dvec[qrow] : 0.f;
+    // dP^T accumulates onto -D (this lane's row), so the products leave dP - D
+    f32x16 negd;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negd[i] = -drow;
 
     const size_t kvoff = ((size_t)b * Hkv + g) * (size_t)Nk * D;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -489,7 +498,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             // S^T = K Q^T and dP^T = V dO^T for 32 keys: lane holds query l32,
             // score rows 8*(i/4) + 4*half + i%4, i.e. the keys of tile rows
             // key0 + 32kb + perm16 of those
-            f32x16 sacc = f32x16{}, pacc = f32x16{};
+            f32x16 sacc = f32x16{}, pacc = negd;
 #pragma unroll
             for (int s = 0; s < D / 16; ++s) {
                 const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&Krb[(kb * 32 + prow) * RS + 16 * s + 8 * half]);
@@ -514,7 +523,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 for (int e = 0; e < 4; ++e) {
                     const int i = 4 * j + e;
                     const float p = fast_exp2(fmaf(sacc[i], scale_log2, -lrow));
-                    ds[e] = p * (pacc[i] - drow);
+                    ds[e] = p * pacc[i];
                 }
                 da[j >> 1][2 * (j & 1)] = pack_bf16x2(ds[0], ds[1]);
                 da[j >> 1][2 * (j & 1) + 1] = pack_bf16x2(ds[2], ds[3]);
