@@ -330,6 +330,30 @@ def cpu_baseline(w3, w4, budget_s=20.0):
 EXTRA = (("mha_d64_n2048", 0), ("gqa_rope_n32768", 0), ("gqa_rope_n8192", 4096), ("gqa_rope_n32768", 4096))
 
 
+PREWARM_S = 0.25  # set from --prewarm-s
+
+
+def timed_calls(torch, stream, call, reps):
+    """Untimed calls for PREWARM_S seconds (the clock settles under load), then
+    ``reps`` calls timed one by one with events on ``stream``; mean ms."""
+    t0 = time.perf_counter()
+    call()
+    torch.cuda.synchronize()
+    while time.perf_counter() - t0 < PREWARM_S:
+        call()
+        torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    return float(np.mean(ms))
+
+
 def extra_prefill(torch, esd, stream, reps=5):
     """TFLOP/s of the other prefill workloads (same entry points, same timing):
     MHA d=64 N=2048, long-context GQA N=32768, and the causal sliding window
@@ -349,20 +373,9 @@ def extra_prefill(torch, esd, stream, reps=5):
         ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda") if nws else None
         call = lambda: esd.fwd(dq, dk, dv, causal=w.causal, scale=w.scale, rope_base=w.rope_base,
                                out=o, lse=lse, workspace=ws, window=win)
-        call()
-        torch.cuda.synchronize()
-        ms = []
-        for _ in range(reps):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            call()
-            b.record(stream)
-            torch.cuda.synchronize()
-            ms.append(a.elapsed_time(b))
+        ms = timed_calls(torch, stream, call, reps)
         fl = fwd_flops(w, win)
-        out[label] = {"workload": note, "flops": fl, "ms": float(np.mean(ms)),
-                     "tflops": fl / (float(np.mean(ms)) * 1e-3) / 1e12}
+        out[label] = {"workload": note, "flops": fl, "ms": ms, "tflops": fl / (ms * 1e-3) / 1e12}
         del dq, dk, dv, o, lse, ws
         torch.cuda.empty_cache()
     return out
@@ -378,20 +391,10 @@ def extra_decode_multi(torch, esd, stream, w, lens, dkc, dvc, dlens, T=4, reps=1
     ws = torch.empty(esd.decode_multi_workspace_bytes(w.B, w.Hq, w.Hkv, T, w.max_len, w.d),
                      dtype=torch.uint8, device="cuda")
     call = lambda: esd.decode_multi(q, dkc, dvc, dlens, scale=w.scale, out=o, lse=lse, workspace=ws)
-    call()
-    torch.cuda.synchronize()
-    ms = []
-    for _ in range(reps):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        call()
-        b.record(stream)
-        torch.cuda.synchronize()
-        ms.append(a.elapsed_time(b))
+    ms = timed_calls(torch, stream, call, reps)
     nb = decode_bytes(w, lens, T)
     return {"workload": f"{w.note}, T={T} new tokens per sequence (bottom-right causal)",
-            "bytes": nb, "ms": float(np.mean(ms)), "gbs": nb / (float(np.mean(ms)) * 1e-3) / 1e9}
+            "bytes": nb, "ms": ms, "gbs": nb / (ms * 1e-3) / 1e9}
 
 
 def extra_decode_paged(torch, esd, stream, w, lens, reps=10):
@@ -406,22 +409,12 @@ def extra_decode_paged(torch, esd, stream, w, lens, reps=10):
     ws = torch.empty(esd.decode_paged_workspace_bytes(w.B, w.Hq, w.Hkv, 1, table.shape[1], 16, w.d),
                      dtype=torch.uint8, device="cuda")
     call = lambda: esd.decode_paged(dq, dkp, dvp, dt, dl, scale=w.scale, out=o, lse=lse, workspace=ws)
-    call()
-    torch.cuda.synchronize()
-    ms = []
-    for _ in range(reps):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        call()
-        b.record(stream)
-        torch.cuda.synchronize()
-        ms.append(a.elapsed_time(b))
+    ms = timed_calls(torch, stream, call, reps)
     nb = decode_bytes(w, lens) + table.size * 4
     del dq, dkp, dvp, dt, dl, o, lse, ws
     torch.cuda.empty_cache()
     return {"workload": f"{w.note}, paged cache in blocks of 16 tokens", "bytes": nb,
-            "ms": float(np.mean(ms)), "gbs": nb / (float(np.mean(ms)) * 1e-3) / 1e9}
+            "ms": ms, "gbs": nb / (ms * 1e-3) / 1e9}
 
 
 def extra_backward(torch, esd, stream, w, reps=5):
@@ -442,22 +435,12 @@ def extra_backward(torch, esd, stream, w, reps=5):
                                              esd.ATTN_BF16), dtype=torch.uint8, device="cuda")
     call = lambda: esd.bwd(dq_, dk_, dv_, o, lse, do, causal=w.causal, scale=w.scale,
                            rope_base=w.rope_base, dq=gq, dk=gk, dv=gv, workspace=ws)
-    call()
-    torch.cuda.synchronize()
-    ms = []
-    for _ in range(reps):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        call()
-        b.record(stream)
-        torch.cuda.synchronize()
-        ms.append(a.elapsed_time(b))
+    ms = timed_calls(torch, stream, call, reps)
     fl = 2.5 * fwd_flops(w)
     del dq_, dk_, dv_, do, o, lse, gq, gk, gv, ws
     torch.cuda.empty_cache()
-    return {"workload": f"{w.note}, backward (dQ, dK, dV)", "flops": fl, "ms": float(np.mean(ms)),
-            "tflops": fl / (float(np.mean(ms)) * 1e-3) / 1e12}
+    return {"workload": f"{w.note}, backward (dQ, dK, dV)", "flops": fl, "ms": ms,
+            "tflops": fl / (ms * 1e-3) / 1e12}
 
 
 def main():
@@ -468,6 +451,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "backward"], default=None,
                     help="time one leg only, or the backward pass alone (for profiling)")
+    ap.add_argument("--prewarm-s", type=float, default=0.25,
+                    help="seconds of untimed steps before the warmup steps: under load the GPU's "
+                         "clock settles over ~50 ms, and steps taken before that run up to 25%% slower")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra prefill workloads (MHA d=64 N=2048, GQA N=32768, sliding window)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -477,6 +463,8 @@ def main():
     ap.add_argument("--write-clock-record", metavar="DIR",
                     help="write profiles/clock.json from rocprofv3 --pmc output under DIR (no GPU)")
     args = ap.parse_args()
+    global PREWARM_S
+    PREWARM_S = args.prewarm_s
     if args.write_traffic_record or args.write_clock_record:
         if args.write_traffic_record:
             write_traffic_record(args.write_traffic_record)
@@ -560,6 +548,13 @@ def main():
             esd.decode(dqd, dkc, dvc, dlens, scale=w4.scale, out=o4, lse=l4, workspace=ws4)
             if evs: evs[3].record(stream)
 
+    print("[bench] prewarm", file=sys.stderr, flush=True)
+    t_pre = time.perf_counter()
+    n_pre = 0
+    while time.perf_counter() - t_pre < args.prewarm_s:
+        step()
+        torch.cuda.synchronize()
+        n_pre += 1
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -610,6 +605,7 @@ def main():
             "prefill_rope_k_ms": rope_avg, "prefill_attention_kernel_ms": attn_ms,
             "prefill_attention_kernel_ms_min": float(np.min(attn_ms_all)),
             "decode_bytes": nbytes, "decode_ms": dec_avg, "decode_ms_min": float(np.min(dec_ms)),
+            "prewarm_steps": n_pre,
         },
         "roofline": {
             # events around the attention kernel's own launch
