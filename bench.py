@@ -43,15 +43,43 @@ CLOCK_RECORD = os.path.join(ROOT, "profiles", "clock.json")
 CSRC = os.path.join(ROOT, "exact_scaled_dot_amd", "csrc")
 
 
+def strip_comments(src: str) -> str:
+    """C/C++ source without its comments (string and character literals kept
+    whole) and without trailing blanks, so that editing a comment leaves the
+    code's hash alone."""
+    out = []
+    i, n = 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = [ln.rstrip() for ln in "".join(out).split("\n")]
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_hash() -> str:
-    """Hash of the kernel sources, to tell whether recorded counters still apply."""
+    """Hash of the kernel sources' code (comments left out), to tell whether
+    recorded counters still apply."""
     import hashlib
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
         if f.endswith((".hip", ".h", ".cpp")):
             h.update(f.encode())
-            with open(os.path.join(CSRC, f), "rb") as fh:
-                h.update(fh.read())
+            with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+                h.update(strip_comments(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

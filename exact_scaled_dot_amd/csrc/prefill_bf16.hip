@@ -30,8 +30,9 @@
 //     used, with one barrier per tile; each tile takes two online-softmax
 //     updates of 32 keys.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: in the 32x32 accumulator a lane
-//     holds one query (column) and 16 keys, so the row max and sum need one
-//     exchange between the two 32-lane halves.
+//     holds one query (column) and 16 keys, so a row lives in two lanes, one in
+//     each 32-lane half.  The halves exchange their maxima only when one of
+//     them may move the row's reference (below), and their sums at the end.
 //   * O^T += V^T P^T on the same MFMA; P goes from the S accumulator into the B
 //     operand without leaving registers (the k-slot order is permuted the same
 //     way in both operands).  V stays row-major in LDS and the A operand is
@@ -40,7 +41,9 @@
 //     and one v_exp_f32 per score.  The reference max m of a row moves only when
 //     the row max exceeds it by more than 8 (a factor 2^8), so most updates skip
 //     the rescale of O and l; O and l always share one reference, so the result
-//     is the same exact recurrence.  O is divided by the sum of the bf16-rounded
+//     is the same exact recurrence.  A lane tests its own 16 scores against the
+//     threshold, and only when some lane of the wave passes it is the row max
+//     formed across the halves and the reference moved.  O is divided by the sum of the bf16-rounded
 //     weights that entered the P V product (a true convex combination of V
 //     rows); the logsumexp uses the fp32 sum.
 //   * causal: a workgroup stops at the last tile its rows can see, a wave skips

@@ -87,3 +87,17 @@ def test_clock_record(tmp_path, monkeypatch):
     assert k["mfma_util_pct"] == pytest.approx(50.0)
     assert "rope_bf16_kernel" not in r["kernels"]
     assert bench.recorded_clock("prefill_bf16_kernel<128, true, true, false>") == pytest.approx(2.0)
+
+
+def test_source_hash_ignores_comments(tmp_path, monkeypatch):
+    src = ('// header\n#include "x.h"\n/* block\n comment */\nint f(int a) {  // trailing\n'
+           '    const char* s = "not // a comment"; return a + \'/\';\n}\n')
+    (tmp_path / "k.hip").write_text(src)
+    monkeypatch.setattr(bench, "CSRC", str(tmp_path))
+    h0 = bench.source_hash()
+    (tmp_path / "k.hip").write_text(src.replace("// trailing", "// reworded").replace("block", "other"))
+    assert bench.source_hash() == h0
+    (tmp_path / "k.hip").write_text(src.replace("a + ", "a - "))
+    assert bench.source_hash() != h0
+    (tmp_path / "k.hip").write_text(src.replace("not // a", "not // b"))   # inside a string: code
+    assert bench.source_hash() != h0
