@@ -27,6 +27,10 @@
 //   * dQ: 8 waves, 32 query rows each, GQA heads sharing K/V tiles of 64
 //     keys: S^T = K Q^T and dP^T = V dO^T, then dQ^T += K^T dS^T with K read
 //     transposed; a wave skips the 32-key halves past its last row (causal).
+// In both, the element mask runs only where an update crosses a diagonal or
+// the end of K (a wave-uniform branch, applied to the scores in place), and
+// the dP accumulator starts from -D, so the products leave dP - D and dS is
+// one multiply.
 // Both stream their tiles through two LDS buffers with one barrier per tile:
 // the next tile is loaded while the current one is computed (dK/dV straight
 // into LDS, dQ through registers).
