@@ -294,10 +294,17 @@ def pin_rounding_vs_torch():
     including values exactly halfway between two bf16 numbers."""
     r = _rng(12)
     x = np.concatenate([r.standard_normal(5000) * 10, r.standard_normal(100) * 1e-30])
-    # halfway cases: bf16 grid point + half an ulp, odd and even neighbours
-    base = _bf16_via_torch(r.standard_normal(200))
-    ulp = np.abs(base) * 2.0 ** -7
-    x = np.concatenate([x, base + ulp / 2, base - ulp / 2])
+    # exact halfway cases: an fp32 whose low 16 bits are 0x8000 lies halfway
+    # between its two bf16 neighbours; upper halves with an even and an odd
+    # last bit, both signs, normal exponents; and the fp32 values one step
+    # either side of each tie
+    hi = r.integers(0x0080, 0x7F00, 400).astype(np.uint32)
+    hi[0::2] &= np.uint32(0xFFFE)
+    hi[1::2] |= np.uint32(1)
+    hi |= r.integers(0, 2, 400).astype(np.uint32) << np.uint32(15)
+    ties = (hi << np.uint32(16)) | np.uint32(0x8000)
+    near = np.concatenate([ties, ties - np.uint32(1), ties + np.uint32(1)])
+    x = np.concatenate([x, near.view(np.float32).astype(np.float64)])
     assert np.array_equal(oa.round_to_dtype(x, "bf16"), _bf16_via_torch(x))
     assert np.array_equal(oa.round_to_dtype(x, "f32"), x.astype(np.float32).astype(np.float64))
     rot = oa.rope(r.standard_normal((4, 8)), np.arange(4), 10000.0, "bf16")

@@ -183,7 +183,39 @@ def _bwd_rows_wrong_group(q, k, v, do, b, g, q_rows, k_rows, **kw):
 
 _orig_bwd_rows = oa.attention_bwd_rows
 
+def _rope_query_at_row_index(x, positions, base, dtype):
+    # queries rotated at their row index i instead of their position Nk - Nq + i
+    # (key positions start at 0 and are left alone)
+    p = np.asarray(positions)
+    if p.size and p.min() > 0:
+        p = p - p.min()
+    return _orig_rope(x, p, base, dtype)
+
+
+_orig_round = oa.round_to_dtype
+
+
+def _softmax_no_max(x):
+    # the naive form: exp of the raw scores (overflows for large scores)
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        e = np.exp(x)
+        return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def _round_ties_away(x, dtype):
+    # bf16 rounding with ties away from zero instead of to the even neighbour
+    if dtype != "bf16":
+        return _orig_round(x, dtype)
+    u = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x8000) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 MUTATIONS = {
+    "rope_query_at_row_index": ("rope", _rope_query_at_row_index),
+    "softmax_no_max_shift": ("softmax", _softmax_no_max),
+    "bf16_ties_away_from_zero": ("round_to_dtype", _round_ties_away),
     "bf16_bits_read_as_fp16": ("_f64", _f64_as_fp16),
     "bwd_rows_wrong_group": ("attention_bwd_rows", _bwd_rows_wrong_group),
     "bwd_rope_not_transposed": ("rope_transpose", _rope_transpose_forward),
