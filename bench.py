@@ -409,6 +409,43 @@ def extra_prefill(torch, esd, stream, reps=5):
     return out
 
 
+def extra_decode_evicted(torch, esd, stream, w, nbytes, dq, dkc, dvc, dlens, o, lse, ws, reps=10):
+    """GB/s of the headline decode call with the 256 MB last-level cache
+    (Infinity Cache) evicted before each call, outside the events, in two ways
+    on the same stream: a 1 GiB write (which leaves that cache full of dirty
+    lines for the call to write back as it streams) and a 1 GiB read.  The
+    back-to-back timing of the headline line may find the tail of the
+    previous call's cache rows still there."""
+    print("[bench] extra workload decode with the last-level cache evicted", file=sys.stderr,
+          flush=True)
+    junk = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    junk.fill_(1)
+    sink = torch.empty((), dtype=torch.int64, device="cuda")
+    call = lambda: esd.decode(dq, dkc, dvc, dlens, scale=w.scale, out=o, lse=lse, workspace=ws)
+    call()
+    out = {"workload": f"{w.note}, a 1 GiB write or read between calls (outside the timed region)",
+           "bytes": nbytes}
+    for how in ("write", "read"):
+        ms = []
+        for r in range(reps):
+            if how == "write":
+                junk.fill_(r & 0xFF)
+            else:
+                torch.sum(junk.view(torch.int32), dim=0, out=sink)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            call()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        m = float(np.mean(ms))
+        out[f"{how}_evict"] = {"ms": m, "ms_min": float(np.min(ms)), "gbs": nbytes / (m * 1e-3) / 1e9}
+    del junk, sink
+    torch.cuda.empty_cache()
+    return out
+
+
 def extra_decode_multi(torch, esd, stream, w, lens, dkc, dvc, dlens, T=4, reps=10):
     """GB/s of multi-token decode on the decode batch: T = 4 new tokens per
     sequence (verifying drafted tokens), so 16 queries per KV head."""
@@ -661,8 +698,11 @@ def main():
         },
     }
     if not args.no_extra and args.only is None:
-        rec["extra_decode"] = {"decode_multi_T4": extra_decode_multi(torch, esd, stream, w4, lens,
-                                                                     dkc, dvc, dlens)}
+        rec["extra_decode"] = {"decode_evicted": extra_decode_evicted(torch, esd, stream, w4, nbytes,
+                                                                      dqd, dkc, dvc, dlens, o4, l4,
+                                                                      ws4)}
+        rec["extra_decode"]["decode_multi_T4"] = extra_decode_multi(torch, esd, stream, w4, lens,
+                                                                    dkc, dvc, dlens)
         del dkc, dvc
         torch.cuda.empty_cache()
         rec["extra_decode"]["decode_paged_bs16"] = extra_decode_paged(torch, esd, stream, w4, lens)

@@ -17,7 +17,9 @@
 //     a wave held in registers and V in the wave's slice of LDS as MFMA
 //     operands, which keeps the wave within 256 registers) and streams
 //     64-query tiles of Q and dO of every query head that reads this KV head
-//     through LDS, so the GQA sum over heads happens in the accumulators.  Each tile
+//     through LDS (all heads of a tile in a row, tiles in an order that keeps
+//     the workgroups of one KV head on the same tile), so the GQA sum over
+//     heads happens in the accumulators.  Each tile
 //     takes two updates of 32 queries between barriers, so the two waves of a
 //     SIMD drift out of phase within a tile; a wave skips an update whose rows
 //     see none of its keys (causal).  Per update and wave: S = Q K^T and
@@ -177,12 +179,12 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) { dka[i] = f32x16{}; dva[i] = f32x16{}; }
 
-    // The loop runs over (query head of the group, query tile) pairs, from the
-    // first tile holding a position >= k0 (causal).  Pair it+1 is loaded into
-    // the other LDS buffer while pair it is computed (per 32-query update: S
-    // and dP, then P and dS, then dV and dK); the buffer parity is a constant
-    // in the loop unrolled by two, so every LDS address is a per-lane base plus
-    // an immediate; one barrier per pair.  Two waves share each SIMD, so one's
+    // The loop runs over (query head of the group, query tile) pairs, the
+    // tiles from the first holding a position >= k0 (causal) to the last.
+    // Pair it+1 is loaded into the other LDS buffer while pair it is computed
+    // (per 32-query update: S and dP, then P and dS, then dV and dK); the
+    // buffer parity is a constant in the loop unrolled by two, so every LDS
+    // address is a per-lane base plus an immediate; one barrier per pair.  Two waves share each SIMD, so one's
     // vector and LDS work overlaps the other's matrix products.
     const int qstart = CAUSAL ? max(0, k0 - off) / kQT * kQT : 0;
     const int ntq = (Nq - qstart + kQT - 1) / kQT;
@@ -212,11 +214,29 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 ((q0 + rr) * D + col) * 2, 0, 0, 0);
         }
     };
-    auto tile_q0 = [&](int it) { return qstart + (it - (it / ntq) * ntq) * kQT; };
+    // Pair it is query head it % G of tile it / G counted from one end: the
+    // heads of a tile follow each other, and the tiles are taken so that the
+    // workgroups of one KV head read the same tile at about the same time.
+    // The first half of the key blocks (one dispatch wave of workgroups at
+    // these sizes) all start together, so they run from the last tile down,
+    // each stopping at its own first tile.  The second half start one by one
+    // as those finish, the last to finish first (it has the fewest tiles), so
+    // they run up from their own first tile: a workgroup that starts later
+    // starts at a later tile, by as many tiles as its start was delayed.
+    // Workgroups go to the eight XCDs in turn, so when B * Hkv is a multiple
+    // of 8 those of one KV head share an XCD and its L2, which then serves
+    // most of their tile reads: 85% L2 hits against 25% when every workgroup
+    // ran up from its own first tile, with 0.8 instead of 3.7 GB fetched from
+    // behind the L2 on the causal GQA N = 8192 backward (2.9% less time).
+    const int nkb = (Nk + kKW * kKeysW - 1) / (kKW * kKeysW);
+    const bool up = kb >= (nkb + 1) / 2;
+    auto tile_of = [&](int tq) { return up ? tq : ntq - 1 - tq; };
+    auto tile_q0 = [&](int it) { return qstart + tile_of(it / G) * kQT; };
     auto gload = [&](int it, int P, Pair& r) {  // pairs past the last repeat it (never used)
         it = min(it, niter - 1);
-        const int hh = it / ntq;
-        const int q0 = qstart + (it - hh * ntq) * kQT;
+        const int tq = it / G;
+        const int hh = it - tq * G;
+        const int q0 = qstart + tile_of(tq) * kQT;
         const size_t qoff = ((size_t)b * Hq + g * G + hh) * (size_t)Nq;
         const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(q + qoff * D), (short)0, Nq * D * 2, 0x00020000);
