@@ -351,7 +351,9 @@ def cpu_baseline(w3, w4, budget_s=20.0):
                   + f"; decode: {len(lens)} of the {w4.B} sequences of the decode workload in "
                   f"{t_dec:.1f} s, the rate over them standing for the workload",
         "extrapolated": heads < total,
-        "decode_value": nbytes / t_dec / 1e9, "decode_unit": "GB/s",
+        "prefill_seconds": t_pf, "prefill_heads": heads,
+        "prefill_seconds_whole_workload": t_pf * total / heads,
+        "decode_value": nbytes / t_dec / 1e9, "decode_unit": "GB/s", "decode_seconds": t_dec,
     }
 
 
@@ -669,7 +671,9 @@ def main():
             "prefill_flops": flops, "prefill_ms": pf_avg, "prefill_ms_min": float(np.min(pf_ms)),
             "prefill_rope_k_ms": rope_avg, "prefill_attention_kernel_ms": attn_ms,
             "prefill_attention_kernel_ms_min": float(np.min(attn_ms_all)),
+            "prefill_attention_kernel_ms_median": float(np.median(attn_ms_all)),
             "decode_bytes": nbytes, "decode_ms": dec_avg, "decode_ms_min": float(np.min(dec_ms)),
+            "decode_ms_median": float(np.median(dec_ms)),
             "prewarm_steps": n_pre,
         },
         "roofline": {
@@ -712,6 +716,9 @@ def main():
         rec["extra"] = extra_prefill(torch, esd, stream)
         rec["extra"]["gqa_rope_n8192_backward"] = extra_backward(torch, esd, stream, w3)
     if cpu is not None:
+        # the GPU figures over the oracle's on the same workloads (context only)
+        cpu["gpu_speedup"] = {"prefill": tflops / cpu["value"] if tflops else None,
+                              "decode": gbs / cpu["decode_value"] if gbs else None}
         rec["cpu_baseline"] = cpu
     print(json.dumps(rec), flush=True)
 
