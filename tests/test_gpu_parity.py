@@ -112,9 +112,11 @@ def test_rope_attention_small(dtype, base, d):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("base,N,off", [(10000.0, 300, 0), (500000.0, 4096, 28672), (10.0, 64, 5)])
+@pytest.mark.parametrize("base,N,off", [(10000.0, 300, 0), (500000.0, 4096, 28672), (10.0, 64, 5),
+                                         (10000.0, 1000, (1 << 22) - 1000)])
 def test_rope_apply_bit_exact(dtype, base, N, off):
-    """The device rotation rounds to exactly the oracle's values."""
+    """The device rotation rounds to exactly the oracle's values, up to the
+    largest position any call accepts (2^22 - 1)."""
     d = 128
     x = W.normal((2, 3, N, d), 7300 + N, 4.0, dtype)
     got = host(esd.rope_apply(dev(x), base, pos_offset=off))
