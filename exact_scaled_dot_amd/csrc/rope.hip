@@ -11,58 +11,98 @@
 
 namespace attn {
 
+// Grid: x covers the N rows of one (batch, head) slice, 256 vectors per
+// workgroup; y walks the slices, kSPT at a time, so each thread has kSPT
+// loads in flight.  Within a slice the vector index is below
+// N * d / 8 <= 2^28 (N <= 2^22, d <= 512), so the row and the position come
+// from 32-bit arithmetic (a shift when d is 64 or 128, VPR != 0); only the
+// slice offset is 64-bit.
+constexpr int kMaxGridY = 65535;
+constexpr int kSPT = 4;  // slices per thread and step
+
 // One thread rotates 8 bf16 (4 pairs) of a row.
+template <int VPR>
 __global__ void __launch_bounds__(256)
-rope_bf16_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ out,
-                 long long nvec, int N, int d, int pos_offset,
-                 const double2* __restrict__ tab) {
-    const int vec_per_row = d >> 3;
-    const int half = d >> 1;
-    for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < nvec;
-         i += (long long)gridDim.x * blockDim.x) {
-        const long long row = i / vec_per_row;
-        const int d0 = (int)(i - row * vec_per_row) << 3;
-        const int pos = pos_offset + (int)(row % N);
-        uint4 v = *reinterpret_cast<const uint4*>(x + row * d + d0);
-        *reinterpret_cast<uint4*>(out + row * d + d0) = rope8_bf16(v, tab + (size_t)pos * half, d0);
+rope_bf16_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ out, long long slices,
+                 int N, int d, int pos_offset, const double2* __restrict__ tab) {
+    const int vpr = VPR ? VPR : d >> 3;  // 16-byte vectors per row
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= N * vpr) return;
+    const int n = i / vpr;
+    const int d0 = (i - n * vpr) << 3;
+    const double2* trow = tab + (size_t)(pos_offset + n) * (d >> 1);
+    // kSPT slices per step, their loads issued before any rotation
+    for (long long s0 = (long long)blockIdx.y * kSPT; s0 < slices; s0 += (long long)gridDim.y * kSPT) {
+        uint4 v[kSPT];
+#pragma unroll
+        for (int j = 0; j < kSPT; ++j)
+            if (s0 + j < slices)
+                v[j] = *reinterpret_cast<const uint4*>(x + ((size_t)(s0 + j) * N + n) * d + d0);
+#pragma unroll
+        for (int j = 0; j < kSPT; ++j)
+            if (s0 + j < slices)
+                *reinterpret_cast<uint4*>(out + ((size_t)(s0 + j) * N + n) * d + d0) =
+                    rope8_bf16(v[j], trow, d0);
     }
 }
 
 // One thread rotates 4 fp32 (2 pairs) of a row.
+template <int VPR>
 __global__ void __launch_bounds__(256)
-rope_f32_kernel(const float* __restrict__ x, float* __restrict__ out, long long nvec, int N,
+rope_f32_kernel(const float* __restrict__ x, float* __restrict__ out, long long slices, int N,
                 int d, int pos_offset, const double2* __restrict__ tab) {
-    const int vec_per_row = d >> 2;
-    const int half = d >> 1;
-    for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < nvec;
-         i += (long long)gridDim.x * blockDim.x) {
-        const long long row = i / vec_per_row;
-        const int d0 = (int)(i - row * vec_per_row) << 2;
-        const int pos = pos_offset + (int)(row % N);
-        float4 v = *reinterpret_cast<const float4*>(x + row * d + d0);
-        *reinterpret_cast<float4*>(out + row * d + d0) = rope4_f32(v, tab + (size_t)pos * half, d0);
+    const int vpr = VPR ? VPR : d >> 2;
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= N * vpr) return;
+    const int n = i / vpr;
+    const int d0 = (i - n * vpr) << 2;
+    const double2* trow = tab + (size_t)(pos_offset + n) * (d >> 1);
+    for (long long s0 = (long long)blockIdx.y * kSPT; s0 < slices; s0 += (long long)gridDim.y * kSPT) {
+        float4 v[kSPT];
+#pragma unroll
+        for (int j = 0; j < kSPT; ++j)
+            if (s0 + j < slices)
+                v[j] = *reinterpret_cast<const float4*>(x + ((size_t)(s0 + j) * N + n) * d + d0);
+#pragma unroll
+        for (int j = 0; j < kSPT; ++j)
+            if (s0 + j < slices)
+                *reinterpret_cast<float4*>(out + ((size_t)(s0 + j) * N + n) * d + d0) =
+                    rope4_f32(v[j], trow, d0);
     }
 }
 
-static int grid_for(long long nvec) {
-    long long g = (nvec + 255) / 256;
-    if (g > 256 * 64) g = 256 * 64;  // grid-stride beyond 64 workgroups per CU
-    return (int)(g < 1 ? 1 : g);
+static dim3 grid_for(long long slices, int N, int vpr) {
+    const long long gx = ((long long)N * vpr + 255) / 256;
+    const long long steps = (slices + kSPT - 1) / kSPT;
+    const long long gy = steps < kMaxGridY ? steps : kMaxGridY;
+    return dim3((unsigned)gx, (unsigned)gy);
 }
 
 hipError_t launch_rope_bf16(const uint16_t* x, uint16_t* out, long long rows, int N, int d,
                             int pos_offset, const double2* tab, hipStream_t stream) {
-    const long long nvec = rows * (d / 8);
-    if (nvec == 0) return hipSuccess;
-    rope_bf16_kernel<<<grid_for(nvec), 256, 0, stream>>>(x, out, nvec, N, d, pos_offset, tab);
+    if (rows == 0 || N == 0) return hipSuccess;
+    const long long slices = rows / N;
+    const dim3 g = grid_for(slices, N, d / 8);
+    if (d == 128)
+        rope_bf16_kernel<16><<<g, 256, 0, stream>>>(x, out, slices, N, d, pos_offset, tab);
+    else if (d == 64)
+        rope_bf16_kernel<8><<<g, 256, 0, stream>>>(x, out, slices, N, d, pos_offset, tab);
+    else
+        rope_bf16_kernel<0><<<g, 256, 0, stream>>>(x, out, slices, N, d, pos_offset, tab);
     return hipGetLastError();
 }
 
 hipError_t launch_rope_f32(const float* x, float* out, long long rows, int N, int d,
                            int pos_offset, const double2* tab, hipStream_t stream) {
-    const long long nvec = rows * (d / 4);
-    if (nvec == 0) return hipSuccess;
-    rope_f32_kernel<<<grid_for(nvec), 256, 0, stream>>>(x, out, nvec, N, d, pos_offset, tab);
+    if (rows == 0 || N == 0) return hipSuccess;
+    const long long slices = rows / N;
+    const dim3 g = grid_for(slices, N, d / 4);
+    if (d == 128)
+        rope_f32_kernel<32><<<g, 256, 0, stream>>>(x, out, slices, N, d, pos_offset, tab);
+    else if (d == 64)
+        rope_f32_kernel<16><<<g, 256, 0, stream>>>(x, out, slices, N, d, pos_offset, tab);
+    else
+        rope_f32_kernel<0><<<g, 256, 0, stream>>>(x, out, slices, N, d, pos_offset, tab);
     return hipGetLastError();
 }
 
