@@ -177,3 +177,35 @@ def test_bwd_gqa_n8192_every_kv_head():
             _grad_check(got[2][b, g, rows], sv, f"{tag} dv ({len(rows)} rows)")
     del got
     torch.cuda.empty_cache()
+
+
+def test_bwd_group8_n8192_peaky():
+    """Causal attention with 8 query heads per KV head (B=1, Hq=16, Hkv=2,
+    N=8192, d=128), RoPE 5e5 and Q, K ~ N(0, 4^2), whose softmax rows are
+    nearly one-hot, as in the long-context workload: 32 key blocks per KV head,
+    each visiting the 8 heads of every query tile, with B * Hkv = 2 (not a
+    multiple of the XCD count).  dQ on sampled query rows of all 16 heads, dK
+    and dV on the same key rows, both KV heads."""
+    import torch
+    B, Hq, Hkv, N, d = 1, 16, 2, 8192, 128
+    scale = 1 / math.sqrt(d)
+    q = W.normal((B, Hq, N, d), 11601, 4.0, "bf16")
+    k = W.normal((B, Hkv, N, d), 11602, 4.0, "bf16")
+    v = W.normal((B, Hkv, N, d), 11603, 1.0, "bf16")
+    do = W.normal((B, Hq, N, d), 11604, 1.0, "f32")
+    say(f"bwd group of 8, peaky: B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} RoPE 5e5")
+    got = _run(q, k, v, do, True, scale, 500000.0)
+    G = Hq // Hkv
+    fixed = [0, 1, 31, 32, 63, 64, 255, 256, 4095, 4096, N - 257, N - 256, N - 65, N - 64,
+             N - 2, N - 1]
+    rng = np.random.default_rng(11605)
+    for g in range(Hkv):
+        rows = np.unique(np.concatenate([fixed, rng.integers(0, N, 8)]))
+        sq, sk, sv = oa.attention_bwd_rows(q, k, v, do, 0, g, rows, rows, causal=True,
+                                           scale=scale, rope_base=500000.0, dtype="bf16")
+        tag = f"bwd group of 8 g={g}"
+        _grad_check(got[0][0, g * G:(g + 1) * G][:, rows], sq, f"{tag} dq ({len(rows)} rows x {G} heads)")
+        _grad_check(got[1][0, g, rows], sk, f"{tag} dk ({len(rows)} rows)")
+        _grad_check(got[2][0, g, rows], sv, f"{tag} dv ({len(rows)} rows)")
+    del got
+    torch.cuda.empty_cache()
