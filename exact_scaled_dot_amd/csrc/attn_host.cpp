@@ -23,13 +23,28 @@ size_t elem_size(attn_dtype t) { return t == ATTN_F32 ? 4 : 2; }
 bool known_dtype(int t) { return t == ATTN_BF16 || t == ATTN_F32; }
 
 bool log_enabled() {
-    static int on = -1;
-    if (on < 0) {
+    // read once; the initialisation of a local static is thread-safe
+    static const bool on = [] {
         const char* s = std::getenv("ATTN_LOG");
-        on = (s && s[0] == '1') ? 1 : 0;
-    }
-    return on == 1;
+        return s != nullptr && s[0] == '1';
+    }();
+    return on;
 }
+
+// Workspace sizes saturate: a product or sum that does not fit in size_t
+// becomes SIZE_MAX, which no workspace can match, so the call that checks it
+// fails with ATTN_ERR_WORKSPACE instead of accepting a wrapped-around size.
+size_t mul_sat(size_t a, size_t b) {
+    size_t r;
+    return __builtin_mul_overflow(a, b, &r) ? SIZE_MAX : r;
+}
+
+size_t add_sat(size_t a, size_t b) {
+    size_t r;
+    return __builtin_add_overflow(a, b, &r) ? SIZE_MAX : r;
+}
+
+size_t align256(size_t x) { return x > SIZE_MAX - 255 ? SIZE_MAX : (x + 255) & ~(size_t)255; }
 
 int fail(int code, const char* what) {
     if (log_enabled()) fprintf(stderr, "[attn] %s: %s\n", attn_status_str(code), what);
@@ -54,7 +69,8 @@ const char* attn_status_str(int status) {
 size_t attn_fwd_workspace_bytes(int B, int Hkv, int Nk, int d, float rope_base, attn_dtype dtype) {
     if (!(rope_base > 0.f) || B <= 0 || Hkv <= 0 || Nk <= 0 || d <= 0 || !known_dtype(dtype))
         return 0;
-    return (size_t)B * Hkv * Nk * d * elem_size(dtype);
+    return mul_sat(mul_sat(mul_sat(mul_sat((size_t)B, (size_t)Hkv), (size_t)Nk), (size_t)d),
+                   elem_size(dtype));
 }
 
 }  // extern "C"
@@ -163,11 +179,10 @@ int attn_prefill_cached(const void* q, const void* k_cache, const void* v_cache,
 // d floats of O then one float of lse, the two arrays 256-byte aligned.
 static size_t decode_ws_bytes(int B, int Hq, int Hkv, int T, int max_len, int d, int chunk) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0 || max_len <= 0 || d <= 0) return 0;
-    const size_t nch = (size_t)(max_len + chunk - 1) / chunk;
-    const size_t rows = (size_t)B * Hq * T * nch;
-    size_t o_bytes = rows * d * sizeof(float);
-    o_bytes = (o_bytes + 255) & ~(size_t)255;
-    return o_bytes + rows * sizeof(float);
+    const size_t nch = ((size_t)max_len + (size_t)chunk - 1) / (size_t)chunk;
+    const size_t rows = mul_sat(mul_sat(mul_sat((size_t)B, (size_t)Hq), (size_t)T), nch);
+    const size_t o_bytes = align256(mul_sat(mul_sat(rows, (size_t)d), sizeof(float)));
+    return add_sat(o_bytes, mul_sat(rows, sizeof(float)));
 }
 
 size_t attn_decode_multi_workspace_bytes(int B, int Hq, int Hkv, int T, int max_len, int d) {
@@ -320,15 +335,18 @@ int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
 // Workspace of attn_bwd, in order (each section 256-byte aligned): dO in bf16
 // [B,Hq,Nq,d], D [B,Hq,Nq] fp32, lse2 [B,Hq,Nq] fp32, then with RoPE the
 // rotated Q [B,Hq,Nq,d] and K [B,Hkv,Nk,d] in bf16.
-static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, float rope_base,
                                 attn_dtype dtype) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0 || dtype != ATTN_BF16)
         return 0;
-    const size_t rows = (size_t)B * Hq * Nq;
-    size_t n = align256(rows * d * 2) + 2 * align256(rows * 4);
-    if (rope_base > 0.f) n += align256(rows * d * 2) + align256((size_t)B * Hkv * Nk * d * 2);
+    const size_t rows = mul_sat(mul_sat((size_t)B, (size_t)Hq), (size_t)Nq);
+    const size_t rows_d2 = align256(mul_sat(mul_sat(rows, (size_t)d), 2));
+    size_t n = add_sat(rows_d2, mul_sat(2, align256(mul_sat(rows, 4))));
+    if (rope_base > 0.f) {
+        const size_t k_d2 = mul_sat(mul_sat(mul_sat(mul_sat((size_t)B, (size_t)Hkv), (size_t)Nk),
+                                            (size_t)d), 2);
+        n = add_sat(add_sat(n, rows_d2), align256(k_d2));
+    }
     return n;
 }
 

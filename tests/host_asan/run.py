@@ -22,7 +22,8 @@ def main(path):
     os.environ["ATTN_SAN_LIB"] = path
     # -s: a sanitizer report goes straight to stderr (the run stops at the first)
     return pytest.main(["-q", "-s", "-p", "no:cacheprovider", "-o", "addopts=",
-                        os.path.join(TESTS, "test_abi.py"), os.path.join(HERE, "check_dispatch.py")])
+                        os.path.join(TESTS, "test_abi.py"), os.path.join(HERE, "check_dispatch.py"),
+                        os.path.join(HERE, "fuzz_args.py")])
 
 
 if __name__ == "__main__":

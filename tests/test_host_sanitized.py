@@ -1,7 +1,8 @@
 """The library's host code (argument checks, workspace sizing, dispatch, the
 RoPE table) built with g++ under AddressSanitizer and UndefinedBehaviorSanitizer
 against the stand-in runtime of host_asan/stubs.cpp, then driven by
-test_abi.py and host_asan/check_dispatch.py in a child process that has the
+test_abi.py, host_asan/check_dispatch.py and host_asan/fuzz_args.py (randomised
+arguments for every entry point) in a child process that has the
 sanitizer runtime preloaded.  Any sanitizer report fails the test.  CPU only."""
 
 import os
