@@ -51,6 +51,11 @@
  * earlier may still read them).
  * Entry points are thread-safe; calls that share a workspace must be ordered by
  * the caller (same stream or events).
+ *
+ * The *_workspace_bytes queries return 0 for arguments the matching call does
+ * not need a workspace for (or rejects), and SIZE_MAX where the size does not
+ * fit in size_t; no workspace matches that, so the call returns
+ * ATTN_ERR_WORKSPACE.
  */
 #ifndef ATTN_H
 #define ATTN_H
