@@ -52,10 +52,10 @@
  * Entry points are thread-safe; calls that share a workspace must be ordered by
  * the caller (same stream or events).
  *
- * The *_workspace_bytes queries return 0 for arguments the matching call does
- * not need a workspace for (or rejects), and SIZE_MAX where the size does not
- * fit in size_t; no workspace matches that, so the call returns
- * ATTN_ERR_WORKSPACE.
+ * The *_workspace_bytes queries return 0 when the call needs no workspace or
+ * an argument they read is out of range (a size below 1, a dtype the call does
+ * not take), and SIZE_MAX where the size does not fit in size_t; no workspace
+ * matches that, so the call returns ATTN_ERR_WORKSPACE.
  */
 #ifndef ATTN_H
 #define ATTN_H
