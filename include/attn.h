@@ -55,7 +55,8 @@
  * The *_workspace_bytes queries return 0 when the call needs no workspace or
  * an argument they read is out of range (a size below 1, a dtype the call does
  * not take), and SIZE_MAX where the size does not fit in size_t; no workspace
- * matches that, so the call returns ATTN_ERR_WORKSPACE.
+ * matches that, so such a call fails (ATTN_ERR_WORKSPACE, unless an argument
+ * check before the workspace check fails first).
  */
 #ifndef ATTN_H
 #define ATTN_H
