@@ -55,13 +55,20 @@ class AttnError(RuntimeError):
 
 
 def lib():
-    """Load libattn.so once; raise if it has not been built."""
+    """Load libattn.so once; raise if it has not been built.
+
+    torch is imported first.  torch ships its own HIP runtime and asks for it
+    by the unversioned name, so if libattn.so (which asks for the versioned
+    name of the system runtime) were loaded first, the process would hold two
+    runtimes and torch's streams and device memory would be foreign to the
+    library's.  Loaded after torch, libattn.so binds to torch's runtime."""
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(
             f"{LIB_PATH} is missing: build it with `python -m exact_scaled_dot_amd.build`")
+    import torch  # noqa: F401  (see above: one HIP runtime in the process)
     _lib = _declare(ctypes.CDLL(LIB_PATH))
     return _lib
 
