@@ -165,3 +165,20 @@ def test_random_decode(case):
     assert np.array_equal(np.isneginf(gl), dead) and np.all(go[dead] == 0), what
     if (~dead).any():
         check(go[~dead], gl[~dead], ro[~dead], rl[~dead], "bf16", what)
+
+
+# A wider sweep from other seeds: 300 forward and window shapes, 60 backward,
+# 100 decode (every case runs the same checks as above).
+@pytest.mark.parametrize("case", _draw(300, seed=9101), ids=lambda c: f"w{c[0]}")
+def test_random_shape_wide(case):
+    test_random_shape(case)
+
+
+@pytest.mark.parametrize("case", _draw_bwd(60, seed=9102), ids=lambda c: f"w{c[0]}")
+def test_random_backward_wide(case):
+    test_random_backward(case)
+
+
+@pytest.mark.parametrize("case", _draw_dec(100, seed=9103), ids=lambda c: f"w{c[0]}")
+def test_random_decode_wide(case):
+    test_random_decode(case)
