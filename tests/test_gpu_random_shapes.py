@@ -168,7 +168,7 @@ def test_random_decode(case):
 
 
 # A wider sweep from other seeds: 300 forward and window shapes, 60 backward,
-# 100 decode (every case runs the same checks as above).
+# 100 decode (every case runs the same checks as above); then longer sequences.
 @pytest.mark.parametrize("case", _draw(300, seed=9101), ids=lambda c: f"w{c[0]}")
 def test_random_shape_wide(case):
     test_random_shape(case)
@@ -182,3 +182,46 @@ def test_random_backward_wide(case):
 @pytest.mark.parametrize("case", _draw_dec(100, seed=9103), ids=lambda c: f"w{c[0]}")
 def test_random_decode_wide(case):
     test_random_decode(case)
+
+
+def _draw_long(n, seed):
+    """Longer sequences (700-3000 keys): many row blocks and tiles, ragged tails."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        Nk = int(rng.integers(700, 3000))
+        causal = bool(rng.random() < 0.7)
+        rope = float(rng.choice([0.0, 10000.0, 500000.0])) if causal else 0.0
+        Nq = int(rng.integers(1, Nk + 1)) if causal else int(rng.integers(1, 3000))
+        window = int(rng.integers(1, Nk + 40)) if causal and rng.random() < 0.4 else 0
+        dtype = "f32" if rng.random() < 0.15 else "bf16"
+        cases.append((i, dtype, d, 1, Hkv * G, Hkv, Nq, Nk, causal, window, rope))
+    return cases
+
+
+def _draw_bwd_long(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2]))
+        G = int(rng.choice([1, 2, 4]))
+        Nk = int(rng.integers(300, 1500))
+        causal = bool(rng.random() < 0.7)
+        Nq = int(rng.integers(1, Nk + 1)) if causal else int(rng.integers(1, 1500))
+        rope = float(rng.choice([0.0, 10000.0])) if causal else 0.0
+        cases.append((i, d, 1, Hkv * G, Hkv, Nq, Nk, causal, rope))
+    return cases
+
+
+@pytest.mark.parametrize("case", _draw_long(120, seed=9201), ids=lambda c: f"l{c[0]}")
+def test_random_shape_long(case):
+    test_random_shape(case)
+
+
+@pytest.mark.parametrize("case", _draw_bwd_long(20, seed=9202), ids=lambda c: f"l{c[0]}")
+def test_random_backward_long(case):
+    test_random_backward(case)
